@@ -1,0 +1,200 @@
+"""ctypes binding of libdemo (include/demo.h): argument marshalling only.
+
+Every computation runs in the HIP kernels of libdemo.so; this module turns
+PyTorch tensors into device pointers and the current HIP stream, and raises
+on error codes.  There is no fallback: if libdemo.so is missing the first call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdemo.so")
+
+ABI_VERSION = 1
+CHUNK = 32
+SCHEME_DCT, SCHEME_RANDOM, SCHEME_STRIDE, SCHEME_DILOCO = 0, 1, 2, 3
+VAL_TERNARY, VAL_F16, VAL_F32 = 0, 1, 2
+OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, EABI = 0, -1, -2, -3, -4, -5
+
+SYMBOLS = ("demo_abi_version", "demo_strerror", "demo_payload_layout", "demo_encode",
+           "demo_decode_apply", "demo_random_select")
+
+
+class DemoError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+class demo_cfg(ctypes.Structure):
+    _fields_ = [
+        ("abi_version", ctypes.c_uint32),
+        ("scheme", ctypes.c_uint32),
+        ("chunk", ctypes.c_uint32),
+        ("k", ctypes.c_uint32),
+        ("period", ctypes.c_uint32),
+        ("sign", ctypes.c_uint32),
+        ("value_fmt", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+        ("beta", ctypes.c_float),
+        ("lr", ctypes.c_float),
+        ("seed", ctypes.c_uint64),
+        ("step", ctypes.c_uint64),
+        ("chunk_offset", ctypes.c_uint64),
+    ]
+
+
+class demo_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("idx_off", "idx_bytes", "nz_off", "neg_off", "plane_bytes",
+                                                "val_off", "val_bytes", "total_bytes")]
+
+    def as_dict(self) -> dict:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+@dataclass
+class Config:
+    """Python view of demo_cfg."""
+
+    scheme: int = SCHEME_DCT
+    k: int = 1
+    period: int = 16
+    sign: int = 1
+    value_fmt: int = VAL_TERNARY
+    beta: float = 0.9
+    lr: float = 1e-3
+    seed: int = 0
+    step: int = 0
+    chunk_offset: int = 0
+    chunk: int = CHUNK
+    abi_version: int = ABI_VERSION
+    reserved: int = 0
+
+    def c(self) -> demo_cfg:
+        return demo_cfg(self.abi_version, self.scheme, self.chunk, self.k, self.period, self.sign,
+                        self.value_fmt, self.reserved, self.beta, self.lr, self.seed, self.step,
+                        self.chunk_offset)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.demo_abi_version.argtypes = []
+        L.demo_abi_version.restype = ctypes.c_int
+        L.demo_strerror.argtypes = [ctypes.c_int]
+        L.demo_strerror.restype = ctypes.c_char_p
+        L.demo_payload_layout.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, ctypes.POINTER(demo_layout)]
+        L.demo_payload_layout.restype = ctypes.c_int
+        L.demo_encode.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, P, P, P, P, P]
+        L.demo_encode.restype = ctypes.c_int
+        L.demo_decode_apply.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, P, P, ctypes.c_uint64,
+                                        ctypes.c_uint32, P]
+        L.demo_decode_apply.restype = ctypes.c_int
+        L.demo_random_select.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, ctypes.c_uint64,
+                                         ctypes.c_uint64, P, P]
+        L.demo_random_select.restype = ctypes.c_int
+        if L.demo_abi_version() != ABI_VERSION:
+            raise RuntimeError("libdemo.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().demo_strerror(code).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != OK:
+        raise DemoError(rc, what)
+
+
+def _ptr(t) -> int | None:
+    """Device (or host) address of a tensor, None for None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _cfg(cfg) -> demo_cfg:
+    return cfg.c() if isinstance(cfg, Config) else cfg
+
+
+# --------------------------------------------------------------------------- #
+# the C ABI, one Python function per entry point                              #
+# --------------------------------------------------------------------------- #
+
+def demo_abi_version() -> int:
+    return int(lib().demo_abi_version())
+
+
+def demo_strerror(code: int) -> str:
+    return strerror(code)
+
+
+def demo_payload_layout(cfg, n_elems: int) -> dict:
+    out = demo_layout()
+    c = _cfg(cfg)
+    _check(lib().demo_payload_layout(ctypes.byref(c), n_elems, ctypes.byref(out)), "demo_payload_layout")
+    return out.as_dict()
+
+
+def demo_encode(cfg, n_elems: int, grad, momentum, payload_out, q_out=None, stream=None) -> None:
+    c = _cfg(cfg)
+    _check(lib().demo_encode(ctypes.byref(c), n_elems, _ptr(grad), _ptr(momentum), _ptr(payload_out),
+                             _ptr(q_out), _stream(stream)), "demo_encode")
+
+
+def demo_decode_apply(cfg, n_elems: int, params, payloads, stride: int, R: int, stream=None) -> None:
+    c = _cfg(cfg)
+    _check(lib().demo_decode_apply(ctypes.byref(c), n_elems, _ptr(params), _ptr(payloads), stride, R,
+                                   _stream(stream)), "demo_decode_apply")
+
+
+def demo_random_select(cfg, seed: int, step: int, n_chunks: int, masks_out, stream=None) -> None:
+    c = _cfg(cfg)
+    _check(lib().demo_random_select(ctypes.byref(c), seed, step, n_chunks, _ptr(masks_out), _stream(stream)),
+           "demo_random_select")
+
+
+# raw return codes (tests of the boundary's validation)
+def raw_encode(cfg, n_elems, grad, momentum, payload_out, q_out=None, stream=0) -> int:
+    c = _cfg(cfg)
+    return int(lib().demo_encode(ctypes.byref(c), n_elems, grad, momentum, payload_out, q_out, stream))
+
+
+def raw_decode_apply(cfg, n_elems, params, payloads, stride, R, stream=0) -> int:
+    c = _cfg(cfg)
+    return int(lib().demo_decode_apply(ctypes.byref(c), n_elems, params, payloads, stride, R, stream))
+
+
+def raw_random_select(cfg, seed, step, n_chunks, masks_out, stream=0) -> int:
+    c = _cfg(cfg)
+    return int(lib().demo_random_select(ctypes.byref(c), seed, step, n_chunks, masks_out, stream))
+
+
+def raw_payload_layout(cfg, n_elems) -> tuple[int, dict]:
+    out = demo_layout()
+    c = _cfg(cfg)
+    rc = int(lib().demo_payload_layout(ctypes.byref(c), n_elems, ctypes.byref(out)))
+    return rc, out.as_dict()

@@ -1,0 +1,650 @@
+// kernels.hpp -- HIP kernels of libdemo for gfx950.
+//
+// Encode (DeToNATION notes, Algorithm 1 steps 3-5) and decode (steps 6-7) of
+// the DeMo / FlexDeMo optimizer step, one wavefront per group of 64 chunks,
+// persistent over the groups of the shard.  Every array is read and written
+// once, in coalesced float4 order; the per-chunk work (transform, selection,
+// packing) runs one chunk per lane on an LDS-transposed copy.
+#pragma once
+
+#include <hip/hip_fp16.h>
+
+#include "device_common.hpp"
+
+namespace demo {
+
+enum { VF_TERNARY = 0, VF_F16 = 1, VF_F32 = 2 };
+
+struct EncArgs {
+    const float* g;
+    float* m;
+    uint8_t* pay;
+    float* q_out;
+    uint64_t n, C, G;
+    uint64_t idx_off, nz_off, neg_off, val_off;
+    uint64_t chunk_offset, seed;
+    uint32_t step_lo;
+    uint32_t mask;  // shared positions of STRIDE / DILOCO
+    float beta;
+    int k;
+    int random;     // 1: positions from random_mask per chunk
+};
+
+struct DecArgs {
+    float* theta;
+    const uint8_t* pay;
+    uint64_t stride;
+    uint64_t n, C, G;
+    uint64_t idx_off, nz_off, neg_off, val_off;
+    uint64_t chunk_offset, seed;
+    uint32_t step_lo;
+    uint32_t mask;
+    float lr, invR;
+    int k, R;
+    int random;
+};
+
+// ---------------------------------------------------------------- streaming --
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// read-once stream (gradients): non-temporal load
+__device__ __forceinline__ float4 load_stream(const float4* p) {
+    const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+// u = beta*m + g for the wave's group, coalesced order; zero beyond n.
+__device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool full, int lane, float4 (&uc)[8]) {
+    if (full) {
+        const float4* g4 = reinterpret_cast<const float4*>(a.g + base);
+        const float4* m4 = reinterpret_cast<const float4*>(a.m + base);
+        float4 gv[8], mv[8];
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            gv[r] = load_stream(g4 + r * kWave + lane);
+            mv[r] = m4[r * kWave + lane];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            uc[r].x = fmaf(a.beta, mv[r].x, gv[r].x);
+            uc[r].y = fmaf(a.beta, mv[r].y, gv[r].y);
+            uc[r].z = fmaf(a.beta, mv[r].z, gv[r].z);
+            uc[r].w = fmaf(a.beta, mv[r].w, gv[r].w);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint64_t e = base + r * 256 + lane * 4 + t;
+                v[t] = (e < a.n) ? fmaf(a.beta, a.m[e], a.g[e]) : 0.f;
+            }
+            uc[r] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// coalesced tile -> LDS (chunk-swizzled)
+__device__ __forceinline__ void put_coalesced(float* st, int lane, const float4 (&v)[8]) {
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        *reinterpret_cast<float4*>(st + swz(8 * r + (lane >> 3), 4 * (lane & 7))) = v[r];
+}
+
+__device__ __forceinline__ void get_coalesced(const float* st, int lane, float4 (&v)[8]) {
+#pragma unroll
+    for (int r = 0; r < 8; r++)
+        v[r] = *reinterpret_cast<const float4*>(st + swz(8 * r + (lane >> 3), 4 * (lane & 7)));
+}
+
+__device__ __forceinline__ void put_chunk(float* st, int lane, const float (&x)[32]) {
+#pragma unroll
+    for (int q = 0; q < 8; q++)
+        *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) =
+            make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+}
+
+__device__ __forceinline__ void get_chunk(const float* st, int lane, float (&x)[32]) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const float4 v = *reinterpret_cast<const float4*>(st + swz(lane, 4 * q));
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+    }
+}
+
+// store a coalesced tile to dst[base ...], guarded beyond n
+__device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint64_t n, bool full, int lane,
+                                           const float4 (&v)[8]) {
+    if (full) {
+        float4* d4 = reinterpret_cast<float4*>(dst + base);
+#pragma unroll
+        for (int r = 0; r < 8; r++) d4[r * kWave + lane] = v[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const float t[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+            for (int s = 0; s < 4; s++) {
+                const uint64_t e = base + r * 256 + lane * 4 + s;
+                if (e < n) dst[e] = t[s];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void fill_basis_table(float* tab) {
+    for (int t = threadIdx.x; t < kChunk * kChunk; t += blockDim.x)
+        tab[(t >> 5) * kTabStride + (t & 31)] = kBasisT[t >> 5][t & 31];
+    __syncthreads();
+}
+
+__device__ __forceinline__ uint16_t f16_of_sign(float v) {
+    return v > 0.f ? (uint16_t)0x3C00u : (v < 0.f ? (uint16_t)0xBC00u : (uint16_t)0u);
+}
+
+// ------------------------------------------------------------ encode (DCT) --
+//
+// KS > 0: k <= KS, selection by k argmax passes, q by sparse inverse
+//         transform from the LDS basis table.
+// KS = 0: any k, selection mask, q by the full inverse transform.
+
+template <int KS, int VF, bool WQ>
+__global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
+    __shared__ float tab[kChunk * kTabStride];
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    if (KS > 0) fill_basis_table(tab);
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    float* st = stage_all + wv * kGroupElems;
+    const int k = a.k;
+
+    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
+         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t base = grp * kGroupElems;
+        const bool full = base + kGroupElems <= a.n;
+        const uint64_t c = grp * kWave + lane;
+        const bool valid = c < a.C;
+
+        float4 uc[8];
+        load_u(a, base, full, lane, uc);
+        wave_lds_sync();
+        put_coalesced(st, lane, uc);
+        wave_lds_sync();
+        float u[32];
+        get_chunk(st, lane, u);
+
+        float X[32];
+        dct32(u, X);
+
+        float q[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) q[i] = 0.f;
+
+        uint64_t mynz = 0, myneg = 0;
+
+        if constexpr (KS > 0) {
+            int selj[KS];
+            float selv[KS];
+            float ax[32];
+#pragma unroll
+            for (int j = 0; j < 32; j++) ax[j] = fabsf(X[j]);
+#pragma unroll
+            for (int p = 0; p < KS; p++) {
+                if (p < k) {
+                    float best = -1.f, bx = 0.f;
+                    int bj = 0;
+#pragma unroll
+                    for (int j = 0; j < 32; j++) {
+                        const bool gt = ax[j] > best;
+                        best = gt ? ax[j] : best;
+                        bx = gt ? X[j] : bx;
+                        bj = gt ? j : bj;
+                    }
+                    selj[p] = bj;
+                    selv[p] = bx;
+                    if (p + 1 < k) {
+#pragma unroll
+                        for (int j = 0; j < 32; j++) ax[j] = (j == bj) ? -1.f : ax[j];
+                    }
+                } else {
+                    selj[p] = kChunk + p;
+                    selv[p] = 0.f;
+                }
+            }
+            // ascending position order
+#pragma unroll
+            for (int pass = 0; pass < KS; pass++) {
+#pragma unroll
+                for (int i = pass & 1; i + 1 < KS; i += 2) {
+                    const bool sw = selj[i] > selj[i + 1];
+                    const int j0 = sw ? selj[i + 1] : selj[i];
+                    const int j1 = sw ? selj[i] : selj[i + 1];
+                    const float v0 = sw ? selv[i + 1] : selv[i];
+                    const float v1 = sw ? selv[i] : selv[i + 1];
+                    selj[i] = j0;
+                    selj[i + 1] = j1;
+                    selv[i] = v0;
+                    selv[i + 1] = v1;
+                }
+            }
+            // q = sum_s X_js * B[js][:]
+#pragma unroll
+            for (int p = 0; p < KS; p++) {
+                if (p < k) {
+                    const float x = selv[p];
+                    const float* t = tab + selj[p];
+#pragma unroll
+                    for (int i = 0; i < 32; i++) q[i] = fmaf(x, t[i * kTabStride], q[i]);
+                }
+            }
+            // payload
+            if (valid) {
+                uint8_t* idx = a.pay + a.idx_off + c * (uint64_t)k;
+                if constexpr (KS == 1) {
+                    idx[0] = (uint8_t)selj[0];
+                } else if constexpr (KS == 2) {
+                    *reinterpret_cast<uint16_t*>(idx) = (uint16_t)(selj[0] | (selj[1] << 8));
+                } else {
+                    if (KS == 4 && k == 4) {
+                        *reinterpret_cast<uint32_t*>(idx) = (uint32_t)selj[0] | ((uint32_t)selj[1] << 8) |
+                                                            ((uint32_t)selj[2] << 16) | ((uint32_t)selj[KS - 1] << 24);
+                    } else {
+#pragma unroll
+                        for (int p = 0; p < KS; p++)
+                            if (p < k) idx[p] = (uint8_t)selj[p];
+                    }
+                }
+                if (VF == VF_F32) {
+                    float* val = reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k;
+#pragma unroll
+                    for (int p = 0; p < KS; p++)
+                        if (p < k) val[p] = sgnf(selv[p]);
+                } else if (VF == VF_F16) {
+                    uint16_t* val = reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k;
+#pragma unroll
+                    for (int p = 0; p < KS; p++)
+                        if (p < k) val[p] = f16_of_sign(selv[p]);
+                }
+            }
+            if (VF == VF_TERNARY) {
+#pragma unroll
+                for (int p = 0; p < KS; p++) {
+                    if (p < k) {
+                        const uint64_t nzb = __ballot(valid && selv[p] != 0.f);
+                        const uint64_t negb = __ballot(valid && selv[p] < 0.f);
+                        if (lane == p) {
+                            mynz = nzb;
+                            myneg = negb;
+                        }
+                    }
+                }
+            }
+        } else {
+            // generic k: k argmax passes build the selection mask
+            float ax[32];
+#pragma unroll
+            for (int j = 0; j < 32; j++) ax[j] = fabsf(X[j]);
+            uint32_t S = 0;
+            for (int p = 0; p < k; p++) {
+                float best = -1.f;
+                int bj = 0;
+#pragma unroll
+                for (int j = 0; j < 32; j++) {
+                    const bool gt = ax[j] > best;
+                    best = gt ? ax[j] : best;
+                    bj = gt ? j : bj;
+                }
+                S |= 1u << bj;
+#pragma unroll
+                for (int j = 0; j < 32; j++) ax[j] = (j == bj) ? -1.f : ax[j];
+            }
+            float Xs[32];
+#pragma unroll
+            for (int j = 0; j < 32; j++) Xs[j] = ((S >> j) & 1u) ? X[j] : 0.f;
+            idct32(Xs, q);
+            // slots in ascending position order
+            uint32_t nzv = 0, negv = 0;
+            int s = 0;
+            uint8_t* idx = a.pay + a.idx_off + c * (uint64_t)k;
+#pragma unroll
+            for (int j = 0; j < 32; j++) {
+                if ((S >> j) & 1u) {
+                    nzv |= (X[j] != 0.f ? 1u : 0u) << s;
+                    negv |= (X[j] < 0.f ? 1u : 0u) << s;
+                    if (valid) {
+                        idx[s] = (uint8_t)j;
+                        if (VF == VF_F32)
+                            (reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = sgnf(X[j]);
+                        else if (VF == VF_F16)
+                            (reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = f16_of_sign(X[j]);
+                    }
+                    s++;
+                }
+            }
+            if (VF == VF_TERNARY) {
+                for (int p = 0; p < k; p++) {
+                    const uint64_t nzb = __ballot(valid && ((nzv >> p) & 1u));
+                    const uint64_t negb = __ballot(valid && ((negv >> p) & 1u));
+                    if (lane == p) {
+                        mynz = nzb;
+                        myneg = negb;
+                    }
+                }
+            }
+        }
+
+        if (VF == VF_TERNARY && lane < k) {
+            reinterpret_cast<uint64_t*>(a.pay + a.nz_off)[grp * (uint64_t)k + lane] = mynz;
+            reinterpret_cast<uint64_t*>(a.pay + a.neg_off)[grp * (uint64_t)k + lane] = myneg;
+        }
+
+        // m <- u - q, back through LDS to coalesced order
+        float mo[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) mo[i] = u[i] - q[i];
+        put_chunk(st, lane, mo);
+        wave_lds_sync();
+        float4 outc[8];
+        get_coalesced(st, lane, outc);
+        store_tile(a.m, base, a.n, full, lane, outc);
+        if constexpr (WQ) {
+            wave_lds_sync();
+            put_chunk(st, lane, q);
+            wave_lds_sync();
+            get_coalesced(st, lane, outc);
+            store_tile(a.q_out, base, a.n, full, lane, outc);
+        }
+    }
+}
+
+// ---------------------------------------- encode (Random / Striding / DiLoCo) --
+
+template <int VF, bool WQ>
+__global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    float* st = stage_all + wv * kGroupElems;
+    const int k = a.k;
+
+    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
+         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t base = grp * kGroupElems;
+        const bool full = base + kGroupElems <= a.n;
+        const uint64_t c = grp * kWave + lane;
+        const bool valid = c < a.C;
+
+        float4 uc[8];
+        load_u(a, base, full, lane, uc);
+        wave_lds_sync();
+        put_coalesced(st, lane, uc);
+        wave_lds_sync();
+        float u[32];
+        get_chunk(st, lane, u);
+
+        const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + c, k) : a.mask;
+
+        uint32_t nzpos = 0, negpos = 0;
+        float mo[32];
+#pragma unroll
+        for (int j = 0; j < 32; j++) {
+            const bool sel = (mask >> j) & 1u;
+            nzpos |= ((sel && u[j] != 0.f) ? 1u : 0u) << j;
+            negpos |= ((sel && u[j] < 0.f) ? 1u : 0u) << j;
+            mo[j] = sel ? 0.f : u[j];
+        }
+        // slot s = s-th selected position in ascending order
+        uint32_t nzv = 0, negv = 0, mm = mask;
+        for (int s = 0; s < k; s++) {
+            const uint32_t j = __builtin_ctz(mm) & 31u;  // mm keeps k set bits for k draws
+            mm &= mm - 1u;
+            nzv |= ((nzpos >> j) & 1u) << s;
+            negv |= ((negpos >> j) & 1u) << s;
+        }
+
+        if (VF == VF_TERNARY) {
+            uint64_t mynz = 0, myneg = 0;
+            for (int s = 0; s < k; s++) {
+                const uint64_t nzb = __ballot(valid && ((nzv >> s) & 1u));
+                const uint64_t negb = __ballot(valid && ((negv >> s) & 1u));
+                if (lane == s) {
+                    mynz = nzb;
+                    myneg = negb;
+                }
+            }
+            if (lane < k) {
+                reinterpret_cast<uint64_t*>(a.pay + a.nz_off)[grp * (uint64_t)k + lane] = mynz;
+                reinterpret_cast<uint64_t*>(a.pay + a.neg_off)[grp * (uint64_t)k + lane] = myneg;
+            }
+        } else if (valid) {
+            for (int s = 0; s < k; s++) {
+                const float v = ((nzv >> s) & 1u) ? (((negv >> s) & 1u) ? -1.f : 1.f) : 0.f;
+                if (VF == VF_F32)
+                    (reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = v;
+                else
+                    (reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = f16_of_sign(v);
+            }
+        }
+
+        put_chunk(st, lane, mo);
+        wave_lds_sync();
+        float4 outc[8];
+        get_coalesced(st, lane, outc);
+        store_tile(a.m, base, a.n, full, lane, outc);
+        if constexpr (WQ) {
+            float q[32];
+#pragma unroll
+            for (int j = 0; j < 32; j++) q[j] = ((mask >> j) & 1u) ? u[j] : 0.f;
+            wave_lds_sync();
+            put_chunk(st, lane, q);
+            wave_lds_sync();
+            get_coalesced(st, lane, outc);
+            store_tile(a.q_out, base, a.n, full, lane, outc);
+        }
+    }
+}
+
+// DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.
+template <bool WQ>
+__global__ __launch_bounds__(kBlock) void momentum_kernel(EncArgs a) {
+    const uint64_t n4 = a.n / 4;
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    const float4* g4 = reinterpret_cast<const float4*>(a.g);
+    float4* m4 = reinterpret_cast<float4*>(a.m);
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const float4 gv = load_stream(g4 + i);
+        float4 mv = m4[i];
+        mv.x = fmaf(a.beta, mv.x, gv.x);
+        mv.y = fmaf(a.beta, mv.y, gv.y);
+        mv.z = fmaf(a.beta, mv.z, gv.z);
+        mv.w = fmaf(a.beta, mv.w, gv.w);
+        m4[i] = mv;
+        if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (a.n & 3)) {
+        const uint64_t e = n4 * 4 + threadIdx.x;
+        a.m[e] = fmaf(a.beta, a.m[e], a.g[e]);
+        if (WQ) a.q_out[e] = 0.f;
+    }
+}
+
+// ------------------------------------------------------------------ decode --
+
+__device__ __forceinline__ float ternary_of(uint64_t nzw, uint64_t negw, int lane) {
+    const bool nz = (nzw >> lane) & 1ull;
+    const bool ng = (negw >> lane) & 1ull;
+    return nz ? (ng ? -1.f : 1.f) : 0.f;
+}
+
+// value of slot s of chunk c (lane) in replica payload pr
+template <int VF>
+__device__ __forceinline__ float slot_value(const DecArgs& a, const uint8_t* pr, uint64_t grp, uint64_t c, int s,
+                                            int lane) {
+    if (VF == VF_TERNARY) {
+        const uint64_t w = grp * (uint64_t)a.k + s;
+        const uint64_t nzw = reinterpret_cast<const uint64_t*>(pr + a.nz_off)[w];
+        const uint64_t negw = reinterpret_cast<const uint64_t*>(pr + a.neg_off)[w];
+        return ternary_of(nzw, negw, lane);
+    } else if (VF == VF_F32) {
+        return reinterpret_cast<const float*>(pr + a.val_off)[c * (uint64_t)a.k + s];
+    } else {
+        return __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(pr + a.val_off)[c * (uint64_t)a.k + s]));
+    }
+}
+
+// theta <- theta - lr * Q with Q in coalesced order from the LDS tile
+__device__ __forceinline__ void apply_update(const DecArgs& a, const float* st, uint64_t base, bool full, int lane) {
+    float4 qc[8];
+    get_coalesced(st, lane, qc);
+    if (full) {
+        float4* t4 = reinterpret_cast<float4*>(a.theta + base);
+        float4 tv[8];
+#pragma unroll
+        for (int r = 0; r < 8; r++) tv[r] = t4[r * kWave + lane];
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            tv[r].x = fmaf(-a.lr, qc[r].x, tv[r].x);
+            tv[r].y = fmaf(-a.lr, qc[r].y, tv[r].y);
+            tv[r].z = fmaf(-a.lr, qc[r].z, tv[r].z);
+            tv[r].w = fmaf(-a.lr, qc[r].w, tv[r].w);
+            t4[r * kWave + lane] = tv[r];
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 8; r++) {
+            const float qq[4] = {qc[r].x, qc[r].y, qc[r].z, qc[r].w};
+#pragma unroll
+            for (int t = 0; t < 4; t++) {
+                const uint64_t e = base + r * 256 + lane * 4 + t;
+                if (e < a.n) a.theta[e] = fmaf(-a.lr, qq[t], a.theta[e]);
+            }
+        }
+    }
+}
+
+// DCT scheme.  Few entries per chunk (R*k <= kSparseEntries): Q accumulated
+// directly from basis rows; otherwise the entries are summed per frequency in
+// LDS and Q is one full inverse transform.
+constexpr int kSparseEntries = 8;
+
+template <int VF>
+__global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
+    __shared__ float tab[kChunk * kTabStride];
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    fill_basis_table(tab);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    float* st = stage_all + wv * kGroupElems;
+    const int k = a.k, R = a.R;
+    const bool sparse = (uint64_t)R * (uint64_t)k <= (uint64_t)kSparseEntries;
+
+    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
+         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t base = grp * kGroupElems;
+        const bool full = base + kGroupElems <= a.n;
+        const uint64_t c = grp * kWave + lane;
+        const bool valid = c < a.C;
+        const uint64_t cv = valid ? c : 0;
+
+        float Q[32];
+        wave_lds_sync();
+        if (sparse) {
+#pragma unroll
+            for (int i = 0; i < 32; i++) Q[i] = 0.f;
+            for (int r = 0; r < R; r++) {
+                const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+                for (int s = 0; s < k; s++) {
+                    const int j = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
+                    const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
+                    const float* t = tab + j;
+#pragma unroll
+                    for (int i = 0; i < 32; i++) Q[i] = fmaf(v, t[i * kTabStride], Q[i]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; q++)
+                *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (valid) {
+                for (int r = 0; r < R; r++) {
+                    const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+                    for (int s = 0; s < k; s++) {
+                        const int j = pr[a.idx_off + c * (uint64_t)k + s] & 31;
+                        const float v = slot_value<VF>(a, pr, grp, c, s, lane);
+                        atomicAdd(st + swz(lane, j), v);
+                    }
+                }
+            }
+            float A[32];
+            get_chunk(st, lane, A);
+            idct32(A, Q);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; i++) Q[i] *= a.invR;
+        put_chunk(st, lane, Q);
+        wave_lds_sync();
+        apply_update(a, st, base, full, lane);
+    }
+}
+
+// Random / Striding / DiLoCo: every replica's slot s sits at the s-th
+// selected position; sums are collected per position in LDS.
+template <int VF>
+__global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
+    float* st = stage_all + wv * kGroupElems;
+    const int k = a.k, R = a.R;
+
+    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
+         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+        const uint64_t base = grp * kGroupElems;
+        const bool full = base + kGroupElems <= a.n;
+        const uint64_t c = grp * kWave + lane;
+        const bool valid = c < a.C;
+        const uint64_t cv = valid ? c : 0;
+        const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + cv, k) : a.mask;
+
+        wave_lds_sync();
+        float acc[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) acc[i] = 0.f;
+        put_chunk(st, lane, acc);
+        for (int r = 0; r < R; r++) {
+            const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+            uint32_t mm = mask;
+            for (int s = 0; s < k; s++) {
+                const uint32_t j = __builtin_ctz(mm) & 31u;  // mm keeps k set bits for k draws
+                mm &= mm - 1u;
+                const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
+                atomicAdd(st + swz(lane, (int)j), v);
+            }
+        }
+        float A[32];
+        get_chunk(st, lane, A);
+#pragma unroll
+        for (int i = 0; i < 32; i++) A[i] *= a.invR;
+        put_chunk(st, lane, A);
+        wave_lds_sync();
+        apply_update(a, st, base, full, lane);
+    }
+}
+
+// ------------------------------------------------------------------ select --
+
+__global__ __launch_bounds__(256) void select_kernel(uint32_t* out, uint64_t n_chunks, uint64_t chunk_offset,
+                                                     uint64_t seed, uint32_t step_lo, int k, int random,
+                                                     uint32_t mask) {
+    for (uint64_t c = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n_chunks;
+         c += (uint64_t)gridDim.x * blockDim.x)
+        out[c] = random ? random_mask(seed, step_lo, chunk_offset + c, k) : mask;
+}
+
+}  // namespace demo

@@ -79,6 +79,8 @@ def lib():
         path = build()
         L = ctypes.CDLL(path)
         P = ctypes.c_void_p
+        L.oracle_threads.argtypes = []
+        L.oracle_threads.restype = ctypes.c_int
         L.oracle_basis.argtypes = [P]
         L.oracle_dct.argtypes = [P, P]
         L.oracle_idct.argtypes = [P, P]
@@ -119,6 +121,11 @@ def _ptr(a: np.ndarray | None):
 # --------------------------------------------------------------------------- #
 # transform, ranking and generator primitives                                 #
 # --------------------------------------------------------------------------- #
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops use."""
+    return int(lib().oracle_threads())
+
 
 def basis() -> np.ndarray:
     B = np.zeros((CHUNK, CHUNK), np.float64)

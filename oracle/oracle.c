@@ -42,6 +42,7 @@
  *  - beta and eta are the fp32 configuration values widened to fp64.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -63,6 +64,9 @@ typedef struct oracle_params {
     uint64_t seed;
     uint64_t step;
 } oracle_params;
+
+/* threads the OpenMP loops below run on */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------ */
 /* DCT-II basis, straight from its definition.                               */

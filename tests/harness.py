@@ -1,0 +1,233 @@
+"""Parity harness: run the HIP library (through its C ABI) and the fp64 oracle
+side by side on the same seeded inputs and compare them.
+
+The comparison rules (what must be bit-exact, where several answers are
+correct, which tolerance applies) are the ones stated for the optimizer step:
+
+* selected positions, ternary signs and the packed payload: bit-exact;
+* a DCT chunk whose k-th and (k+1)-th largest |coefficient| differ by less
+  than NEAR times the chunk's largest |coefficient| (oracle fp64 values) has
+  more than one correct selection: it passes if the GPU's k positions are a
+  valid top-k to that tolerance, is counted, and is left out of the state
+  comparisons from then on (its trajectory legitimately differs);
+* a selected value within NEAR of zero (relative to the chunk's largest
+  magnitude) may take either sign, likewise counted and left out;
+* momentum m and extracted q: max |gpu - oracle| over a chunk divided by that
+  chunk's max |u| must be <= TOL; parameters theta: divided by the chunk's
+  max |theta|.  A chunk whose scale is 0 must match exactly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+from communication_compressed_optimizer_elt_amd import binding as L
+
+TOL = 1e-5
+NEAR = 1e-6
+CHUNK = 32
+
+
+def oracle_params(cfg: L.Config) -> oracle.Params:
+    return oracle.Params(scheme=cfg.scheme, k=cfg.k, period=cfg.period, sign=cfg.sign,
+                         value_fmt=cfg.value_fmt, beta=cfg.beta, lr=cfg.lr, seed=cfg.seed, step=cfg.step)
+
+
+@dataclass
+class Report:
+    steps: int = 0
+    chunks_checked: int = 0
+    near_ties: int = 0
+    sign_exceptions: int = 0
+    max_err_m: float = 0.0
+    max_err_q: float = 0.0
+    max_err_theta: float = 0.0
+    payload_bytes_compared: int = 0
+    failures: list = field(default_factory=list)
+
+    def ok(self) -> bool:
+        return not self.failures and max(self.max_err_m, self.max_err_q, self.max_err_theta) <= TOL
+
+    def summary(self) -> str:
+        return (f"steps={self.steps} chunks={self.chunks_checked} near_ties={self.near_ties} "
+                f"sign_exc={self.sign_exceptions} err_m={self.max_err_m:.3g} err_q={self.max_err_q:.3g} "
+                f"err_theta={self.max_err_theta:.3g} payload_bytes={self.payload_bytes_compared} "
+                f"failures={len(self.failures)}" + ("" if not self.failures else f" first: {self.failures[0]}"))
+
+
+def _chunk_rows(t, n, sample):
+    """Rows [len(sample)][32] (fp32, host) of a flat device tensor, tail zero-padded."""
+    import torch
+
+    C = (n + CHUNK - 1) // CHUNK
+    if n % CHUNK:
+        pad = torch.zeros(C * CHUNK, dtype=t.dtype, device=t.device)
+        pad[:n] = t[:n]
+        t2 = pad.view(C, CHUNK)
+    else:
+        t2 = t[:n].view(C, CHUNK)
+    idx = torch.as_tensor(sample, dtype=torch.long, device=t.device)
+    return t2.index_select(0, idx).cpu().numpy()
+
+
+class ParityRun:
+    """R replicas of one shard on one GPU (replica 0 is this GPU's own), with a
+    shared theta, mirrored by R oracle shards over a chunk sample."""
+
+    def __init__(self, cfg: L.Config, n: int, R: int, sample=None, with_q: bool = False, device="cuda"):
+        import torch
+
+        self.torch = torch
+        self.cfg = cfg
+        self.n = n
+        self.R = R
+        self.C = (n + CHUNK - 1) // CHUNK
+        self.sample = np.arange(self.C) if sample is None else np.unique(np.asarray(sample, np.int64))
+        self.full = len(self.sample) == self.C
+        self.with_q = with_q
+        self.device = device
+        self.layout = L.demo_payload_layout(cfg, n)
+        self.stride = self.layout["total_bytes"]
+        self.pay = torch.zeros(R * self.stride, dtype=torch.uint8, device=device)
+        self.m = [None] * R
+        self.theta = None
+        self.q = [torch.zeros(n, dtype=torch.float32, device=device) for _ in range(R)] if with_q else None
+        self.nvalid = np.full(len(self.sample), CHUNK, np.int32)
+        last = self.sample == self.C - 1
+        self.nvalid[last] = n - (self.C - 1) * CHUNK
+        self.excluded = np.zeros(len(self.sample), bool)
+        self.report = Report()
+        self.shards = None
+
+    def set_state(self, m0_list, theta0):
+        """m0_list: R flat fp32 device tensors; theta0: flat fp32 device tensor."""
+        self.m = [m.clone() for m in m0_list]
+        self.theta = theta0.clone()
+        ids = self.sample.astype(np.uint64) + np.uint64(self.cfg.chunk_offset)
+        th_rows = _chunk_rows(self.theta, self.n, self.sample)
+        self.shards = [oracle.Shard(ids, self.nvalid, _chunk_rows(m, self.n, self.sample), th_rows)
+                       for m in self.m]
+
+    # ------------------------------------------------------------------ #
+    def step(self, t: int, grads, check: bool = True, decode: bool = True):
+        torch = self.torch
+        cfg = self.cfg
+        cfg.step = t
+        for r in range(self.R):
+            L.demo_encode(cfg, self.n, grads[r], self.m[r], self.pay[r * self.stride:],
+                          self.q[r] if self.with_q else None)
+        if decode:
+            L.demo_decode_apply(cfg, self.n, self.theta, self.pay, self.stride, self.R)
+        torch.cuda.synchronize()
+
+        p = oracle_params(cfg)
+        outs = []
+        for r in range(self.R):
+            g_rows = _chunk_rows(grads[r], self.n, self.sample)
+            outs.append(self.shards[r].encode(p, g_rows))
+        if decode:
+            # theta is shared by the replicas; the oracle keeps it in shard 0
+            self.shards[0].decode(p, [o[0] for o in outs], [o[1] for o in outs])
+        self.report.steps += 1
+        if check:
+            self._compare(p, outs, decode)
+        return outs
+
+    # ------------------------------------------------------------------ #
+    def _compare(self, p, outs, decode):
+        torch = self.torch
+        rep = self.report
+        slots = oracle.slots(p)
+        sends = slots > 0
+        for r in range(self.R):
+            idx_o, val_o, q_o, X_o = outs[r]
+            if sends:
+                buf = self.pay[r * self.stride:(r + 1) * self.stride].cpu().numpy()
+                gi, gv, well_formed = oracle.unpack(p, self.n, buf[: self.layout["total_bytes"]])
+                if not well_formed:
+                    rep.failures.append(f"replica {r}: malformed payload (NEG without NZ or bits past the end)")
+                gi = gi[self.sample]
+                gv = gv[self.sample]
+                if p.scheme == oracle.DCT:
+                    same = np.all(gi == idx_o, axis=1) & np.all(gv == val_o, axis=1)
+                else:
+                    same = np.all(gv == val_o, axis=1)
+                for i in np.nonzero(~same)[0]:
+                    self._diagnose(p, r, i, gi[i], gv[i], idx_o[i], val_o[i], X_o[i])
+                if self.full and np.all(same):
+                    ref = oracle.pack(p, self.n, idx_o if p.scheme == oracle.DCT else
+                                      np.zeros_like(idx_o), val_o)
+                    if not np.array_equal(buf[: ref.size], ref):
+                        bad = np.nonzero(buf[: ref.size] != ref)[0]
+                        rep.failures.append(f"replica {r}: payload bytes differ at {bad[:8].tolist()}")
+                    rep.payload_bytes_compared += ref.size
+            keep = ~self.excluded
+            # momentum
+            m_gpu = _chunk_rows(self.m[r], self.n, self.sample).astype(np.float64)
+            m_or = self.shards[r].m
+            u = m_or + q_o
+            scale = np.max(np.abs(u), axis=1)
+            rep.max_err_m = max(rep.max_err_m, _scaled_err(m_gpu, m_or, scale, keep, self.nvalid, rep, f"m[{r}]"))
+            if self.with_q:
+                q_gpu = _chunk_rows(self.q[r], self.n, self.sample).astype(np.float64)
+                rep.max_err_q = max(rep.max_err_q, _scaled_err(q_gpu, q_o, scale, keep, self.nvalid, rep, f"q[{r}]"))
+        if decode:
+            keep = ~self.excluded
+            th_gpu = _chunk_rows(self.theta, self.n, self.sample).astype(np.float64)
+            th_or = self.shards[0].theta
+            scale = np.max(np.abs(th_or), axis=1)
+            rep.max_err_theta = max(rep.max_err_theta,
+                                    _scaled_err(th_gpu, th_or, scale, keep, self.nvalid, rep, "theta"))
+        rep.chunks_checked += int(np.sum(~self.excluded))
+
+    def _diagnose(self, p, r, i, gi, gv, io, vo, X):
+        """A chunk whose slots differ: a near-tie or a near-zero sign, or a failure."""
+        rep = self.report
+        a = np.abs(X)
+        top = np.max(a) if a.size else 0.0
+        k = len(io)
+        if p.scheme == oracle.DCT:
+            sel = [int(j) for j in gi]
+            if len(set(sel)) != k or any(j < 0 or j >= CHUNK for j in sel) or sel != sorted(sel):
+                rep.failures.append(f"replica {r} chunk {self.sample[i]}: invalid positions {sel}")
+                return
+            kth = np.sort(a)[::-1][k - 1]
+            if np.min(a[sel]) < kth - NEAR * top:
+                rep.failures.append(f"replica {r} chunk {self.sample[i]}: gpu {sel} vs oracle {list(io)} "
+                                    f"|X| gpu-min {np.min(a[sel]):.9g} kth {kth:.9g}")
+                return
+            vals = X[sel]
+        else:
+            pos = list(io)
+            vals = X[pos]
+        for s in range(k):
+            want = np.sign(vals[s])
+            if gv[s] != want and not abs(vals[s]) <= NEAR * top:
+                rep.failures.append(f"replica {r} chunk {self.sample[i]} slot {s}: sign {gv[s]} vs {want}")
+                return
+        if p.scheme == oracle.DCT and list(gi) != list(io):
+            rep.near_ties += 1
+        else:
+            rep.sign_exceptions += 1
+        self.excluded[i] = True
+
+
+def _scaled_err(gpu, ref, scale, keep, nvalid, rep, what):
+    valid = np.arange(CHUNK)[None, :] < nvalid[:, None]
+    diff = np.where(valid, np.abs(gpu - ref), 0.0)
+    worst = 0.0
+    zero = scale == 0.0
+    if np.any(zero & keep):
+        bad = np.nonzero(zero & keep & (np.max(diff, axis=1) != 0.0))[0]
+        if bad.size:
+            rep.failures.append(f"{what}: chunk row {bad[0]} has zero scale but nonzero difference")
+    nz = keep & ~zero
+    if np.any(nz):
+        err = np.max(diff[nz], axis=1) / scale[nz]
+        worst = float(np.max(err))
+        if worst > TOL:
+            rows = np.nonzero(nz)[0][np.argsort(-err)[:3]]
+            rep.failures.append(f"{what}: relative error {worst:.3g} at chunk rows {rows.tolist()}")
+    return worst

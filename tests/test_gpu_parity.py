@@ -1,0 +1,314 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Small shards are compared on every chunk (and the packed payload byte for
+byte); full-size shards (the ViT-B set and the OLMo2-1B half shard) in the
+launch configuration the benchmark uses are compared on a fixed chunk sample,
+which is exact rather than approximate because every chunk's trajectory
+depends only on its own inputs and on (seed, step, chunk id).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+
+from harness import TOL, ParityRun  # noqa: E402
+
+import oracle  # noqa: E402
+from communication_compressed_optimizer_elt_amd import binding as L  # noqa: E402
+from communication_compressed_optimizer_elt_amd import synth  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    L.lib()  # fails loudly when libdemo.so is missing
+    return torch
+
+
+def _host_state(torch, n, R, seed_base=0, m_std=1.0, g_std=1.0, theta_std=0.02):
+    """Seeded replica states drawn on the host (numpy), moved to the GPU."""
+    dev = "cuda"
+    m0 = [torch.from_numpy(synth.normal_np(n, m_std, seed_base + r, synth.TAG_MOM)).to(dev) if m_std else
+          torch.zeros(n, dtype=torch.float32, device=dev) for r in range(R)]
+    th = torch.from_numpy(synth.normal_np(n, theta_std, seed_base, synth.TAG_THETA)).to(dev)
+
+    def grads(t):
+        return [torch.from_numpy(synth.normal_np(n, g_std, seed_base + r, synth.TAG_GRAD, t)).to(dev)
+                for r in range(R)]
+
+    return m0, th, grads
+
+
+def _run(torch, cfg, n, R, steps, start=0, sample=None, with_q=True, **state_kw):
+    run = ParityRun(cfg, n, R, sample=sample, with_q=with_q)
+    m0, th, grads = _host_state(torch, n, R, **state_kw)
+    run.set_state(m0, th)
+    for t in range(start, start + steps):
+        run.step(t, grads(t))
+    print(run.report.summary(), flush=True)
+    assert run.report.ok(), run.report.summary()
+    return run
+
+
+# ------------------------------------------------------------- small shards --
+
+def test_config1_demo_k4_r2(torch_cuda):
+    """4096 elements, grad and momentum N(0,1) (seed 0; replica 1 from seed 1),
+    theta N(0, 0.02), beta 0.9, lr 1e-3, k = 4, R = 2, one step."""
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=4)
+    run = _run(torch_cuda, cfg, 4096, 2, 1)
+    assert run.report.payload_bytes_compared > 0
+
+
+@pytest.mark.parametrize("n", [7, 32, 4099, 32 * 64 * 3 + 5, 65536])
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 8, 9, 16, 32])
+def test_dct_shapes_and_k(torch_cuda, n, k):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=k)
+    _run(torch_cuda, cfg, n, 2, 3)
+
+
+@pytest.mark.parametrize("fmt", [L.VAL_TERNARY, L.VAL_F16, L.VAL_F32])
+@pytest.mark.parametrize("R", [1, 3, 9])
+@pytest.mark.parametrize("k", [1, 2, 4, 12])
+def test_dct_formats_and_replicas(torch_cuda, fmt, R, k):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=k, value_fmt=fmt)
+    _run(torch_cuda, cfg, 32 * 64 * 2 + 96, R, 2)
+
+
+def test_dct_chunk_offset_and_large_step(torch_cuda):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=2, chunk_offset=123457)
+    _run(torch_cuda, cfg, 10000, 2, 2, start=2**31 - 1)
+
+
+@pytest.mark.parametrize("fmt", [L.VAL_TERNARY, L.VAL_F16, L.VAL_F32])
+@pytest.mark.parametrize("k", [1, 8, 16, 31, 32])
+def test_random_scheme(torch_cuda, fmt, k):
+    cfg = L.Config(scheme=L.SCHEME_RANDOM, k=k, value_fmt=fmt, seed=2024, chunk_offset=77)
+    _run(torch_cuda, cfg, 32 * 64 * 3 + 17, 2, 3)
+
+
+@pytest.mark.parametrize("fmt", [L.VAL_TERNARY, L.VAL_F16, L.VAL_F32])
+@pytest.mark.parametrize("k", [1, 4, 8, 16, 32])
+def test_stride_scheme(torch_cuda, fmt, k):
+    cfg = L.Config(scheme=L.SCHEME_STRIDE, k=k, value_fmt=fmt)
+    _run(torch_cuda, cfg, 32 * 64 * 2 + 40, 2, 5)
+
+
+@pytest.mark.parametrize("fmt", [L.VAL_TERNARY, L.VAL_F32])
+@pytest.mark.parametrize("period", [1, 4, 16])
+def test_diloco_scheme(torch_cuda, fmt, period):
+    cfg = L.Config(scheme=L.SCHEME_DILOCO, period=period, value_fmt=fmt)
+    _run(torch_cuda, cfg, 32 * 64 * 2 + 3, 2, 17 if period == 16 else 6)
+
+
+def test_zero_and_constant_chunks(torch_cuda):
+    """All-zero chunks (every coefficient ties: positions 0..k-1, sign 0) and
+    constant chunks (only the DC term survives)."""
+    torch = torch_cuda
+    n = 32 * 256
+    for k in (1, 2, 4, 32):
+        cfg = L.Config(scheme=L.SCHEME_DCT, k=k)
+        run = ParityRun(cfg, n, 1, with_q=True)
+        z = torch.zeros(n, dtype=torch.float32, device="cuda")
+        run.set_state([z], z)
+        g = torch.zeros(n, dtype=torch.float32, device="cuda")
+        g.view(-1, 32)[1::3] = 0.5
+        g.view(-1, 32)[2::3] = -2.0
+        run.step(0, [g])
+        print(k, run.report.summary())
+        assert run.report.ok(), run.report.summary()
+
+
+def test_degenerate_k32_extracts_everything(torch_cuda):
+    torch = torch_cuda
+    n = 32 * 64 * 4
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=32)
+    run = _run(torch, cfg, n, 1, 1)
+    u_scale = run.shards[0].m  # oracle m is ~0 (fp64 rounding)
+    assert np.max(np.abs(u_scale)) < 1e-12
+    assert float(run.m[0].abs().max()) < 1e-5
+
+
+def test_select_masks_bit_exact(torch_cuda):
+    torch = torch_cuda
+    n_chunks = 50000
+    out = torch.zeros(n_chunks, dtype=torch.int32, device="cuda")
+    for seed, step, off, k in ((0, 0, 0, 8), (7, 99, 19990560, 16), (2**40 + 3, 2**31, 5, 1), (1, 2, 0, 32)):
+        cfg = L.Config(scheme=L.SCHEME_RANDOM, k=k, chunk_offset=off)
+        L.demo_random_select(cfg, seed, step, n_chunks, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint32)
+        sample = np.r_[0:2000, n_chunks - 2000:n_chunks, 2000:n_chunks - 2000:97]
+        ref = np.array([oracle.select_mask(seed, step, off + int(c), k) for c in sample], np.uint32)
+        assert np.array_equal(got[sample], ref), (seed, step, off, k)
+        assert np.all(np.array([bin(int(x)).count("1") for x in got[:5000]]) == k)
+    for k in (1, 2, 4, 8, 16, 32):
+        cfg = L.Config(scheme=L.SCHEME_STRIDE, k=k)
+        for step in (0, 1, 3, 17):
+            L.demo_random_select(cfg, 0, step, 1000, out)
+            torch.cuda.synchronize()
+            assert np.all(out[:1000].cpu().numpy().view(np.uint32) == oracle.stride_mask(step, k))
+
+
+def test_encode_decode_are_deterministic(torch_cuda):
+    torch = torch_cuda
+    n = 32 * 64 * 40 + 11
+    outs = []
+    for _ in range(2):
+        cfg = L.Config(scheme=L.SCHEME_DCT, k=2)
+        run = ParityRun(cfg, n, 2, sample=np.arange(4), with_q=True)
+        m0, th, grads = _host_state(torch, n, 2)
+        run.set_state(m0, th)
+        for t in range(3):
+            run.step(t, grads(t), check=False)
+        outs.append((run.m[0].cpu().numpy().tobytes(), run.theta.cpu().numpy().tobytes(),
+                     run.pay.cpu().numpy().tobytes()))
+    assert outs[0] == outs[1]
+
+
+# --------------------------------------------------------- full-size shards --
+
+def _sample(C, every, edge):
+    return np.unique(np.r_[0:min(edge, C), max(0, C - edge):C, 0:C:every])
+
+
+def _device_state(torch, segs, R, g_std, theta_std=0.02, scales=None):
+    n = synth.shard_numel(segs)
+    m0 = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(R)]
+    th = synth.normal_torch(n, theta_std, 0, synth.TAG_THETA)
+    if scales is None:
+        scales = np.ones(max(s.group for s in segs) + 1, np.float32)
+    gbuf = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(R)]
+
+    def grads(t):
+        for r in range(R):
+            synth.scaled_grad_torch(segs, scales, g_std, r, t, out=gbuf[r])
+        return gbuf
+
+    return n, m0, th, grads
+
+
+def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None, full_first=0):
+    n, m0, th, grads = _device_state(torch, segs, R, g_std, scales=scales)
+    C = n // 32
+    run = ParityRun(cfg, n, R, sample=_sample(C, sample_every, edge), with_q=False)
+    run.set_state(m0, th)
+    for t in range(steps):
+        run.step(t, grads(t))
+    print(run.report.summary(), flush=True)
+    assert run.report.ok(), run.report.summary()
+    assert run.report.near_ties + run.report.sign_exceptions <= max(3, len(run.sample) // 10000)
+    del run, m0, th
+    torch.cuda.empty_cache()
+
+
+def test_config2_vit_b_set_10_steps(torch_cuda):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    _run_full(torch_cuda, cfg, synth.vit_b_set(), 2, 10, 61, 8192, 1e-2)
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_config3_olmo2_half_shard(torch_cuda, k):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=k)
+    segs = synth.olmo2_half_shard()
+    scales = synth.layer_scales(0, 18)
+    _run_full(torch_cuda, cfg, segs, 2, 100 if k == 1 else 5, 997, 4096, 1e-3, scales=scales)
+
+
+@pytest.mark.parametrize("scheme,k,fmt", [
+    (L.SCHEME_RANDOM, 8, L.VAL_TERNARY), (L.SCHEME_RANDOM, 16, L.VAL_TERNARY),
+    (L.SCHEME_RANDOM, 8, L.VAL_F16), (L.SCHEME_RANDOM, 8, L.VAL_F32),
+    (L.SCHEME_STRIDE, 8, L.VAL_TERNARY), (L.SCHEME_STRIDE, 16, L.VAL_TERNARY),
+])
+def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt)
+    segs = synth.olmo2_half_shard()
+    _run_full(torch_cuda, cfg, segs, 2, 3, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
+
+
+def test_config4_olmo2_half_shard_diloco(torch_cuda):
+    cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16)
+    segs = synth.olmo2_half_shard()
+    _run_full(torch_cuda, cfg, segs, 2, 17, 4999, 2048, 1e-3, scales=synth.layer_scales(0, 18))
+
+
+@pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
+def test_config5_decode_64_replicas(torch_cuda, scheme, k):
+    """Receiver side at R = 64: replica r's payload is the step-0 encode of a
+    state drawn from seed r; the shard then decodes the 64 payloads."""
+    torch = torch_cuda
+    segs = synth.olmo2_half_shard()
+    n = synth.shard_numel(segs)
+    C = n // 32
+    R = 64
+    cfg = L.Config(scheme=scheme, k=k)
+    scales = synth.layer_scales(0, 18)
+    sample = _sample(C, 4999, 1024)
+    lay = L.demo_payload_layout(cfg, n)
+    stride = lay["total_bytes"]
+    pay = torch.zeros(R * stride, dtype=torch.uint8, device="cuda")
+    m = torch.empty(n, dtype=torch.float32, device="cuda")
+    g = torch.empty(n, dtype=torch.float32, device="cuda")
+    th = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
+    from harness import _chunk_rows, oracle_params
+
+    p = oracle_params(cfg)
+    nvalid = np.full(len(sample), 32, np.int32)
+    ids = sample.astype(np.uint64)
+    shard = oracle.Shard(ids, nvalid, np.zeros((len(sample), 32), np.float32), _chunk_rows(th, n, sample))
+    idx_l, val_l = [], []
+    for r in range(R):
+        m.zero_()
+        synth.scaled_grad_torch(segs, scales, 1e-3, r, 0, out=g)
+        L.demo_encode(cfg, n, g, m, pay[r * stride:])
+        torch.cuda.synchronize()
+        peer = oracle.Shard(ids, nvalid, np.zeros((len(sample), 32), np.float32), np.zeros((len(sample), 32), np.float32))
+        i_o, v_o, _, _ = peer.encode(p, _chunk_rows(g, n, sample))
+        gi, gv, ok = oracle.unpack(p, n, pay[r * stride:(r + 1) * stride].cpu().numpy())
+        assert ok
+        same = np.all(gv[sample] == v_o, axis=1)
+        if scheme == L.SCHEME_DCT:
+            same &= np.all(gi[sample] == i_o, axis=1)
+        assert np.mean(same) > 0.9999, r
+        keep = same if r == 0 else keep & same
+        idx_l.append(i_o)
+        val_l.append(v_o)
+    for t in range(3):
+        cfg.step = 0  # the payloads are step-0 payloads; Random positions use step 0
+        L.demo_decode_apply(cfg, n, th, pay, stride, R)
+        torch.cuda.synchronize()
+        shard.decode(p, idx_l, val_l)
+        got = _chunk_rows(th, n, sample).astype(np.float64)
+        ref = shard.theta
+        err = np.max(np.abs(got - ref), axis=1) / np.max(np.abs(ref), axis=1)
+        assert np.max(err[keep]) <= TOL, (t, float(np.max(err[keep])))
+    del pay, m, g, th
+    torch.cuda.empty_cache()
+
+
+def test_full_size_feedback_identity(torch_cuda):
+    """u = m' + q on every element of the OLMo2-1B half shard (q from the
+    library's diagnostic output), the property that holds at any size."""
+    torch = torch_cuda
+    segs = synth.olmo2_half_shard()
+    n = synth.shard_numel(segs)
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    g = synth.scaled_grad_torch(segs, synth.layer_scales(0, 18), 1e-3, 0, 0)
+    m = synth.normal_torch(n, 1e-3, 0, synth.TAG_MOM)
+    u = torch.addcmul(g, m, torch.full_like(m, 0.9))  # beta*m + g in fp32
+    q = torch.empty_like(m)
+    pay = torch.zeros(L.demo_payload_layout(cfg, n)["total_bytes"], dtype=torch.uint8, device="cuda")
+    L.demo_encode(cfg, n, g, m, pay, q)
+    torch.cuda.synchronize()
+    scale = u.view(-1, 32).abs().amax(dim=1, keepdim=True).clamp_min(1e-30)
+    err = ((m + q - u).view(-1, 32).abs() / scale).max().item()
+    assert err <= 1e-6, err
+    del g, m, u, q, pay
+    torch.cuda.empty_cache()
