@@ -3,7 +3,6 @@
 // include/demo.h.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -16,7 +15,6 @@ using demo::DecArgs;
 using demo::EncArgs;
 
 constexpr uint64_t kMaxElems = (uint64_t)1 << 40;  // 4 TB of fp32 per array
-constexpr int kBlocksPerCU = 4;
 
 uint64_t up256(uint64_t x) { return (x + 255u) & ~(uint64_t)255u; }
 
@@ -90,26 +88,19 @@ bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// Compute units of the current device, cached per device id.
-int cu_count() {
-    static std::atomic<int> cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < 64) {
-        int v = cache[dev].load(std::memory_order_relaxed);
-        if (v > 0) return v;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
-    return cus;
+// One block of 4 waves per 4 consecutive groups; the grid covers the shard
+// once (a one-pass grid streams markedly faster than persistent blocks on
+// MI355X).
+unsigned grid_for_groups(uint64_t G) {
+    return (unsigned)((G + demo::kWavesPerBlock - 1) / demo::kWavesPerBlock);
 }
 
-unsigned grid_for_groups(uint64_t G) {
-    const uint64_t blocks = (G + demo::kWavesPerBlock - 1) / demo::kWavesPerBlock;
-    const uint64_t cap = (uint64_t)cu_count() * kBlocksPerCU;
-    return (unsigned)(blocks < cap ? blocks : cap);
-}
+// The encode kernels stream 16 KB of loads per wave (g and m); measured on
+// MI355X they run fastest with 2 blocks (8 waves) per CU, while the decode
+// kernels (8 KB per wave) run fastest at the 4 blocks per CU their own LDS
+// allows.  Reserving this much extra LDS per encode block holds the encode at
+// 2 blocks per CU (160 KB of LDS per CU).
+constexpr size_t kEncodeLdsReserve = 24 * 1024;
 
 uint32_t stride_mask(uint64_t step, uint32_t n) {
     const uint32_t s = 32 / n;
@@ -131,9 +122,11 @@ int launch_status() { return hipGetLastError() == hipSuccess ? DEMO_OK : DEMO_EH
 template <int KS, int VF>
 void launch_encode_dct_q(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true>), dim3(grid), dim3(demo::kBlock), 0, s, a);
+        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+                           s, a);
     else
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false>), dim3(grid), dim3(demo::kBlock), 0, s, a);
+        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+                           s, a);
 }
 
 template <int VF>
@@ -152,9 +145,11 @@ void launch_encode_dct(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) 
 template <int VF>
 void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true>), dim3(grid), dim3(demo::kBlock), 0, s, a);
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve, s,
+                           a);
     else
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false>), dim3(grid), dim3(demo::kBlock), 0, s, a);
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve, s,
+                           a);
 }
 
 }  // namespace
@@ -228,11 +223,7 @@ int demo_encode(const demo_cfg* cfg, uint64_t n_elems, const float* grad, float*
     const bool wq = q_out != nullptr;
 
     if (!sends) {
-        const uint64_t n4 = n_elems / 4;
-        uint64_t blocks = (n4 + 255) / 256;
-        const uint64_t cap = (uint64_t)cu_count() * 8;
-        if (blocks > cap) blocks = cap;
-        if (blocks == 0) blocks = 1;
+        const uint64_t blocks = (n_elems / 4 + 3 + 255) / 256;
         if (wq)
             hipLaunchKernelGGL((demo::momentum_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
         else
@@ -321,8 +312,7 @@ int demo_random_select(const demo_cfg* cfg, uint64_t seed, uint64_t step, uint64
     const int random = cfg->scheme == DEMO_SCHEME_RANDOM;
     const uint32_t mask = random ? 0u : stride_mask(step, cfg->k);
     uint64_t blocks = (n_chunks + 255) / 256;
-    const uint64_t cap = (uint64_t)cu_count() * 16;
-    if (blocks > cap) blocks = cap;
+    if (blocks > (1u << 20)) blocks = 1u << 20;
     hipLaunchKernelGGL(demo::select_kernel, dim3((unsigned)blocks), dim3(256), 0,
                        static_cast<hipStream_t>(hip_stream), masks_out, n_chunks, cfg->chunk_offset, seed,
                        (uint32_t)step, (int)cfg->k, random, mask);

@@ -1,10 +1,11 @@
 // kernels.hpp -- HIP kernels of libdemo for gfx950.
 //
 // Encode (DeToNATION notes, Algorithm 1 steps 3-5) and decode (steps 6-7) of
-// the DeMo / FlexDeMo optimizer step, one wavefront per group of 64 chunks,
-// persistent over the groups of the shard.  Every array is read and written
-// once, in coalesced float4 order; the per-chunk work (transform, selection,
-// packing) runs one chunk per lane on an LDS-transposed copy.
+// the DeMo / FlexDeMo optimizer step.  One wavefront owns one group of 64
+// chunks and a block of 4 waves takes 4 consecutive groups; the grid covers the
+// shard once.  Every array is read and written once, in coalesced float4
+// order; the per-chunk work (transform, selection, packing) runs one chunk per
+// lane on an LDS-transposed copy.
 #pragma once
 
 #include <hip/hip_fp16.h>
@@ -160,12 +161,13 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
     if (KS > 0) fill_basis_table(tab);
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k;
 
-    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
-         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+    {
+        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
+        if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
         const uint64_t c = grp * kWave + lane;
@@ -369,12 +371,13 @@ template <int VF, bool WQ>
 __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k;
 
-    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
-         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+    {
+        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
+        if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
         const uint64_t c = grp * kWave + lane;
@@ -450,15 +453,16 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
     }
 }
 
-// DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.
+// DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.  One
+// float4 per thread; the threads past the last float4 take the 0-3 trailing
+// elements.
 template <bool WQ>
-__global__ __launch_bounds__(kBlock) void momentum_kernel(EncArgs a) {
+__global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
     const uint64_t n4 = a.n / 4;
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    const float4* g4 = reinterpret_cast<const float4*>(a.g);
-    float4* m4 = reinterpret_cast<float4*>(a.m);
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-        const float4 gv = load_stream(g4 + i);
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n4) {
+        const float4 gv = load_stream(reinterpret_cast<const float4*>(a.g) + i);
+        float4* m4 = reinterpret_cast<float4*>(a.m);
         float4 mv = m4[i];
         mv.x = fmaf(a.beta, mv.x, gv.x);
         mv.y = fmaf(a.beta, mv.y, gv.y);
@@ -466,9 +470,8 @@ __global__ __launch_bounds__(kBlock) void momentum_kernel(EncArgs a) {
         mv.w = fmaf(a.beta, mv.w, gv.w);
         m4[i] = mv;
         if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (blockIdx.x == 0 && threadIdx.x < (a.n & 3)) {
-        const uint64_t e = n4 * 4 + threadIdx.x;
+    } else if (i - n4 < (a.n & 3)) {
+        const uint64_t e = n4 * 4 + (i - n4);
         a.m[e] = fmaf(a.beta, a.m[e], a.g[e]);
         if (WQ) a.q_out[e] = 0.f;
     }
@@ -539,13 +542,14 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     fill_basis_table(tab);
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
     const bool sparse = (uint64_t)R * (uint64_t)k <= (uint64_t)kSparseEntries;
 
-    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
-         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+    {
+        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
+        if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
         const uint64_t c = grp * kWave + lane;
@@ -599,12 +603,13 @@ template <int VF>
 __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     const int lane = threadIdx.x & (kWave - 1);
-    const int wv = threadIdx.x / kWave;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    for (uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv; grp < a.G;
-         grp += (uint64_t)gridDim.x * kWavesPerBlock) {
+    {
+        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
+        if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
         const uint64_t c = grp * kWave + lane;

@@ -154,9 +154,10 @@ class ParityRun:
                     same = np.all(gi == idx_o, axis=1) & np.all(gv == val_o, axis=1)
                 else:
                     same = np.all(gv == val_o, axis=1)
-                for i in np.nonzero(~same)[0]:
+                # chunks already left out after a near-tie follow their own trajectory
+                for i in np.nonzero(~same & ~self.excluded)[0]:
                     self._diagnose(p, r, i, gi[i], gv[i], idx_o[i], val_o[i], X_o[i])
-                if self.full and np.all(same):
+                if self.full and np.all(same) and not np.any(self.excluded):
                     ref = oracle.pack(p, self.n, idx_o if p.scheme == oracle.DCT else
                                       np.zeros_like(idx_o), val_o)
                     if not np.array_equal(buf[: ref.size], ref):
