@@ -31,17 +31,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 METRIC = "params/s and HBM GB/s (% of peak) of DeMo encode+decode, OLMo2-1B half shard"
 
+# name: (shard, scheme, k, value format, replicas R, mode); mode "step" = encode + decode
+# per step, "decode" = decode only (R payloads produced before timing)
 WORKLOADS = {
-    # name: (scheme, k, value_fmt, R)
-    "olmo2-1b-half-shard-demo-k1": ("dct", 1, "ternary", 2),
-    "olmo2-1b-half-shard-demo-k2": ("dct", 2, "ternary", 2),
-    "olmo2-1b-half-shard-random-n8": ("random", 8, "ternary", 2),
-    "olmo2-1b-half-shard-random-n16": ("random", 16, "ternary", 2),
-    "olmo2-1b-half-shard-random-n8-f16": ("random", 8, "f16", 2),
-    "olmo2-1b-half-shard-random-n8-f32": ("random", 8, "f32", 2),
-    "olmo2-1b-half-shard-stride-n8": ("stride", 8, "ternary", 2),
-    "vit-b-set-demo-k1": ("dct", 1, "ternary", 2),
+    "olmo2-1b-half-shard-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-demo-k2": ("olmo2", "dct", 2, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-random-n8": ("olmo2", "random", 8, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-random-n16": ("olmo2", "random", 16, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-random-n8-f16": ("olmo2", "random", 8, "f16", 2, "step"),
+    "olmo2-1b-half-shard-random-n8-f32": ("olmo2", "random", 8, "f32", 2, "step"),
+    "olmo2-1b-half-shard-random-n16-f16": ("olmo2", "random", 16, "f16", 2, "step"),
+    "olmo2-1b-half-shard-random-n16-f32": ("olmo2", "random", 16, "f32", 2, "step"),
+    "olmo2-1b-half-shard-stride-n8": ("olmo2", "stride", 8, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-stride-n16": ("olmo2", "stride", 16, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-diloco-p16": ("olmo2", "diloco", 32, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-decode-r64-demo-k1": ("olmo2", "dct", 1, "ternary", 64, "decode"),
+    "olmo2-1b-half-shard-decode-r64-random-n8": ("olmo2", "random", 8, "ternary", 64, "decode"),
+    "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
 }
+DILOCO_PERIOD = 16
 
 
 def source_hash() -> str:
@@ -81,31 +89,38 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    scheme_name, k, fmt_name, R = WORKLOADS[args.workload]
-    scheme = {"dct": L.SCHEME_DCT, "random": L.SCHEME_RANDOM, "stride": L.SCHEME_STRIDE}[scheme_name]
+    shard, scheme_name, k, fmt_name, R, mode = WORKLOADS[args.workload]
+    scheme = {"dct": L.SCHEME_DCT, "random": L.SCHEME_RANDOM, "stride": L.SCHEME_STRIDE,
+              "diloco": L.SCHEME_DILOCO}[scheme_name]
     fmt = {"ternary": L.VAL_TERNARY, "f16": L.VAL_F16, "f32": L.VAL_F32}[fmt_name]
-    segs = synth.vit_b_set() if args.workload.startswith("vit") else synth.olmo2_half_shard()
+    segs = synth.vit_b_set() if shard == "vit" else synth.olmo2_half_shard()
     n = synth.shard_numel(segs)
     scales = synth.layer_scales(0, max(s.group for s in segs) + 1)
-    g_std = 1e-2 if args.workload.startswith("vit") else 1e-3
+    g_std = 1e-2 if shard == "vit" else 1e-3
 
-    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, beta=0.9, lr=1e-3, seed=0, step=0)
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, beta=0.9, lr=1e-3, seed=0, step=0,
+                   period=DILOCO_PERIOD)
     lay = L.demo_payload_layout(cfg, n)
     stride = lay["total_bytes"]
     payload_bytes = lay["idx_bytes"] + 2 * lay["plane_bytes"] + lay["val_bytes"]
+
+    def sends(t):
+        return scheme != L.SCHEME_DILOCO or t % DILOCO_PERIOD == DILOCO_PERIOD - 1
 
     # ---- inputs, resident in HBM -------------------------------------------
     g = synth.scaled_grad_torch(segs, scales, g_std, 0, 0)
     m = torch.zeros(n, dtype=torch.float32, device=dev)
     theta = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
     pay = torch.zeros(R * stride, dtype=torch.uint8, device=dev)
-    # replicas 1..R-1: payloads encoded from states drawn from seeds 1..R-1
+    # the other replicas' payloads: the encode of states drawn from their own
+    # seeds (decode-only workloads: all R replicas, seeds 0..R-1)
     pg = torch.empty_like(g)
     pm = torch.empty_like(m)
-    for r in range(1, R):
+    sync_cfg = L.Config(**{**cfg.__dict__, "step": DILOCO_PERIOD - 1})
+    for r in range(1 if mode == "step" else 0, R):
         synth.scaled_grad_torch(segs, scales, g_std, r, 0, out=pg)
         pm.zero_()
-        L.demo_encode(cfg, n, pg, pm, pay[r * stride:])
+        L.demo_encode(sync_cfg, n, pg, pm, pay[r * stride:])
     torch.cuda.synchronize()
     del pg, pm
     torch.cuda.empty_cache()
@@ -126,46 +141,52 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     stream = torch.cuda.current_stream()
+    # per timed call: (kind, start event, end event, algorithmic bytes)
+    calls = []
 
-    def step(t, ev=None):
+    def timed(kind, nbytes, fn, record):
+        if record:
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            fn()
+            eb.record(stream)
+            calls.append((kind, ea, eb, nbytes))
+        else:
+            fn()
+
+    def step(t, record):
         cfg.step = t
-        if ev is not None:
-            ev[0].record(stream)
-        L.demo_encode(cfg, n, g, m, pay, None, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        L.demo_decode_apply(cfg, n, theta, pay, stride, R, stream)
-        if ev is not None:
-            ev[2].record(stream)
+        # decode-only workloads decode the step-0 payloads (Random positions of step 0)
+        dcfg = cfg if mode == "step" else L.Config(**{**cfg.__dict__, "step": 0})
+        if mode == "step":
+            enc_bytes = 12 * n + (payload_bytes if sends(t) else 0)
+            timed("encode", enc_bytes, lambda: L.demo_encode(cfg, n, g, m, pay, None, stream), record)
+        if sends(t):
+            timed("decode", 8 * n + R * payload_bytes,
+                  lambda: L.demo_decode_apply(dcfg, n, theta, pay, stride, R, stream), record)
 
     for t in range(args.warmup):
-        step(t)
+        step(t, False)
     torch.cuda.synchronize()
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    total_bytes = 0
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, evs[i])
+        step(args.warmup + i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    enc_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    dec_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     step_ms = wall * 1e3 / args.steps
-    enc_bytes = 12 * n + payload_bytes
-    dec_bytes = 8 * n + R * payload_bytes
-    enc_gbps = enc_bytes / (enc_ms.mean() / 1e3) / 1e9
-    dec_gbps = dec_bytes / (dec_ms.mean() / 1e3) / 1e9
-    step_gbps = (enc_bytes + dec_bytes) / (step_ms / 1e3) / 1e9
 
-    kern = {
-        "encode": {"avg_ms": float(enc_ms.mean()), "min_ms": float(enc_ms.min()), "bytes": enc_bytes,
-                   "gbps": enc_gbps},
-        "decode": {"avg_ms": float(dec_ms.mean()), "min_ms": float(dec_ms.min()), "bytes": dec_bytes,
-                   "gbps": dec_gbps},
-    }
-    dom = "encode" if enc_ms.mean() >= dec_ms.mean() else "decode"
+    kern = {}
+    for kind in ("encode", "decode"):
+        ms = np.array([ea.elapsed_time(eb) for kd, ea, eb, _ in calls if kd == kind])
+        nb = [b for kd, _, _, b in calls if kd == kind]
+        if len(ms) == 0:
+            continue
+        total_bytes += sum(nb)
+        kern[kind] = {"calls": len(ms), "avg_ms": float(ms.mean()), "min_ms": float(ms.min()),
+                      "bytes": float(np.mean(nb)), "gbps": float(sum(nb) / (ms.sum() / 1e3) / 1e9)}
+    step_gbps = total_bytes / args.steps / (step_ms / 1e3) / 1e9
+    dom = max(kern, key=lambda kd: kern[kd]["avg_ms"] * kern[kd]["calls"])
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{dom}_{args.workload}.json")
     if os.path.exists(tfile):
@@ -188,7 +209,7 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_elems": n, "scheme": scheme_name, "k": k,
-                   "value_fmt": fmt_name, "replicas": R, "chunk": 32},
+                   "value_fmt": fmt_name, "replicas": R, "chunk": 32, "mode": mode},
         "hbm_gbps": step_gbps,
         "pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "copy_gbps": copy_gbps,
@@ -198,7 +219,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
 
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and mode == "step" and scheme != L.SCHEME_DILOCO:
         def peer_grad(r):
             return synth.scaled_grad_torch(segs, scales, g_std, r, 0)
 

@@ -365,6 +365,38 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
     }
 }
 
+// Ternary slot values (bit s of nzv / negv) of chunk c as fp32 or fp16
+// numbers, 16-byte stores where k allows.
+template <int VF>
+__device__ __forceinline__ void store_slot_values(uint8_t* val, uint64_t c, int k, uint32_t nzv, uint32_t negv) {
+    auto value = [&](int s) { return ((nzv >> s) & 1u) ? (((negv >> s) & 1u) ? -1.f : 1.f) : 0.f; };
+    if (VF == VF_F32) {
+        float* v = reinterpret_cast<float*>(val) + c * (uint64_t)k;
+        if ((k & 3) == 0) {
+#pragma unroll
+            for (int s = 0; s < 32; s += 4)
+                if (s < k) *reinterpret_cast<float4*>(v + s) = make_float4(value(s), value(s + 1), value(s + 2), value(s + 3));
+        } else {
+            for (int s = 0; s < k; s++) v[s] = value(s);
+        }
+    } else {
+        uint16_t* v = reinterpret_cast<uint16_t*>(val) + c * (uint64_t)k;
+        if ((k & 7) == 0) {
+#pragma unroll
+            for (int s = 0; s < 32; s += 8)
+                if (s < k) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int t = 0; t < 4; t++)
+                        w[t] = (uint32_t)f16_of_sign(value(s + 2 * t)) | ((uint32_t)f16_of_sign(value(s + 2 * t + 1)) << 16);
+                    *reinterpret_cast<uint4*>(v + s) = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+        } else {
+            for (int s = 0; s < k; s++) v[s] = f16_of_sign(value(s));
+        }
+    }
+}
+
 // ---------------------------------------- encode (Random / Striding / DiLoCo) --
 
 template <int VF, bool WQ>
@@ -426,13 +458,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
                 reinterpret_cast<uint64_t*>(a.pay + a.neg_off)[grp * (uint64_t)k + lane] = myneg;
             }
         } else if (valid) {
-            for (int s = 0; s < k; s++) {
-                const float v = ((nzv >> s) & 1u) ? (((negv >> s) & 1u) ? -1.f : 1.f) : 0.f;
-                if (VF == VF_F32)
-                    (reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = v;
-                else
-                    (reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = f16_of_sign(v);
-            }
+            store_slot_values<VF>(a.pay + a.val_off, c, k, nzv, negv);
         }
 
         put_chunk(st, lane, mo);
@@ -478,6 +504,56 @@ __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
 }
 
 // ------------------------------------------------------------------ decode --
+
+// Words of a payload, which no kernel of the launch writes, read through the
+// constant address space: wave-uniform addresses become scalar loads.
+__device__ __forceinline__ uint64_t load_const_u64(const uint8_t* base, uint64_t word) {
+    typedef const __attribute__((address_space(4))) uint64_t* const_u64_ptr;
+    return ((const_u64_ptr)base)[word];
+}
+
+// k slot values of chunk c in a value-format payload (fp32 / fp16), added to A
+template <int VF>
+__device__ __forceinline__ void add_slot_values(const uint8_t* val, uint64_t c, int k, float (&A)[32]) {
+    if (VF == VF_F32) {
+        const float* v = reinterpret_cast<const float*>(val) + c * (uint64_t)k;
+        if ((k & 3) == 0) {
+#pragma unroll
+            for (int s = 0; s < 32; s += 4)
+                if (s < k) {
+                    const float4 x = *reinterpret_cast<const float4*>(v + s);
+                    A[s] += x.x;
+                    A[s + 1] += x.y;
+                    A[s + 2] += x.z;
+                    A[s + 3] += x.w;
+                }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 32; s++)
+                if (s < k) A[s] += v[s];
+        }
+    } else {
+        const uint16_t* v = reinterpret_cast<const uint16_t*>(val) + c * (uint64_t)k;
+        if ((k & 7) == 0) {
+#pragma unroll
+            for (int s = 0; s < 32; s += 8)
+                if (s < k) {
+                    const uint4 x = *reinterpret_cast<const uint4*>(v + s);
+                    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+                    for (int t = 0; t < 4; t++) {
+                        A[s + 2 * t] += __half2float(__ushort_as_half((uint16_t)(w[t] & 0xFFFFu)));
+                        A[s + 2 * t + 1] += __half2float(__ushort_as_half((uint16_t)(w[t] >> 16)));
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int s = 0; s < 32; s++)
+                if (s < k) A[s] += __half2float(__ushort_as_half(v[s]));
+        }
+    }
+}
+
 
 __device__ __forceinline__ float ternary_of(uint64_t nzw, uint64_t negw, int lane) {
     const bool nz = (nzw >> lane) & 1ull;
@@ -575,15 +651,32 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
 #pragma unroll
             for (int q = 0; q < 8; q++)
                 *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (valid) {
-                for (int r = 0; r < R; r++) {
-                    const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
-                    for (int s = 0; s < k; s++) {
-                        const int j = pr[a.idx_off + c * (uint64_t)k + s] & 31;
-                        const float v = slot_value<VF>(a, pr, grp, c, s, lane);
-                        atomicAdd(st + swz(lane, j), v);
+            // entries in batches of 8: all loads of a batch go out before its LDS adds
+            const int ne = R * k;
+            for (int e0 = 0; e0 < ne; e0 += 8) {
+                int jj[8];
+                float vv[8];
+#pragma unroll
+                for (int b = 0; b < 8; b++) {
+                    jj[b] = 0;
+                    vv[b] = 0.f;
+                    const int e = e0 + b;
+                    if (e < ne) {
+                        const int rr = e / k, s = e - rr * k;
+                        const uint8_t* pr = a.pay + (uint64_t)rr * a.stride;
+                        jj[b] = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
+                        if (VF == VF_TERNARY) {
+                            const uint64_t w = grp * (uint64_t)k + s;
+                            vv[b] = ternary_of(load_const_u64(pr + a.nz_off, w), load_const_u64(pr + a.neg_off, w),
+                                               lane);
+                        } else {
+                            vv[b] = slot_value<VF>(a, pr, grp, cv, s, lane);
+                        }
                     }
                 }
+#pragma unroll
+                for (int b = 0; b < 8; b++)
+                    if (e0 + b < ne && valid) atomicAdd(st + swz(lane, jj[b]), vv[b]);
             }
             float A[32];
             get_chunk(st, lane, A);
@@ -597,8 +690,11 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     }
 }
 
-// Random / Striding / DiLoCo: every replica's slot s sits at the s-th
-// selected position; sums are collected per position in LDS.
+// Random / Striding / DiLoCo: every replica's slot s sits at the s-th selected
+// position, so the replicas are summed per slot in registers first (ternary
+// planes: wave-uniform 64-chunk words, scalar loads; value formats: the lane's
+// own k values), then each slot sum is written once to its position in the
+// lane's LDS tile and the tile updates theta in coalesced order.
 template <int VF>
 __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
@@ -607,39 +703,46 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    {
-        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
-        if (grp >= a.G) return;
-        const uint64_t base = grp * kGroupElems;
-        const bool full = base + kGroupElems <= a.n;
-        const uint64_t c = grp * kWave + lane;
-        const bool valid = c < a.C;
-        const uint64_t cv = valid ? c : 0;
-        const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + cv, k) : a.mask;
+    const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
+    if (grp >= a.G) return;
+    const uint64_t base = grp * kGroupElems;
+    const bool full = base + kGroupElems <= a.n;
+    const uint64_t c = grp * kWave + lane;
+    const bool valid = c < a.C;
+    const uint64_t cv = valid ? c : 0;
+    const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + cv, k) : a.mask;
 
-        wave_lds_sync();
-        float acc[32];
+    float A[32];
 #pragma unroll
-        for (int i = 0; i < 32; i++) acc[i] = 0.f;
-        put_chunk(st, lane, acc);
-        for (int r = 0; r < R; r++) {
-            const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
-            uint32_t mm = mask;
-            for (int s = 0; s < k; s++) {
-                const uint32_t j = __builtin_ctz(mm) & 31u;  // mm keeps k set bits for k draws
-                mm &= mm - 1u;
-                const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
-                atomicAdd(st + swz(lane, (int)j), v);
-            }
+    for (int s = 0; s < 32; s++) A[s] = 0.f;
+    for (int r = 0; r < R; r++) {
+        const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+        if (VF == VF_TERNARY) {
+#pragma unroll
+            for (int s = 0; s < 32; s++)
+                if (s < k) {
+                    const uint64_t w = grp * (uint64_t)k + s;
+                    A[s] += ternary_of(load_const_u64(pr + a.nz_off, w), load_const_u64(pr + a.neg_off, w), lane);
+                }
+        } else {
+            add_slot_values<VF>(pr + a.val_off, cv, k, A);
         }
-        float A[32];
-        get_chunk(st, lane, A);
-#pragma unroll
-        for (int i = 0; i < 32; i++) A[i] *= a.invR;
-        put_chunk(st, lane, A);
-        wave_lds_sync();
-        apply_update(a, st, base, full, lane);
     }
+
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < 8; q++)
+        *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint32_t mm = mask;
+#pragma unroll
+    for (int s = 0; s < 32; s++)
+        if (s < k) {
+            const uint32_t j = __builtin_ctz(mm) & 31u;  // mm keeps k set bits for k draws
+            mm &= mm - 1u;
+            st[swz(lane, (int)j)] = valid ? A[s] * a.invR : 0.f;
+        }
+    wave_lds_sync();
+    apply_update(a, st, base, full, lane);
 }
 
 // ------------------------------------------------------------------ select --
