@@ -43,7 +43,7 @@ int check_cfg(const demo_cfg* cfg) {
     }
     if (cfg->value_fmt > DEMO_VAL_F32) return DEMO_EINVAL;
     if (cfg->sign > 1) return DEMO_EINVAL;
-    if (cfg->sign == 0) return DEMO_EUNSUPPORTED;
+    if (cfg->sign == 0 && cfg->value_fmt == DEMO_VAL_TERNARY) return DEMO_EINVAL;
     if (!std::isfinite(cfg->beta) || !std::isfinite(cfg->lr)) return DEMO_EINVAL;
     return DEMO_OK;
 }
@@ -152,6 +152,11 @@ void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) 
                            a);
 }
 
+// Selection-scheme decode with ternary planes: up to this many payload entries
+// per chunk (R*k) the plane words are read as wave-uniform scalar loads; beyond
+// it they are staged through LDS with coalesced vector loads.
+constexpr uint64_t kSelScalarEntries = 8;
+
 }  // namespace
 
 extern "C" {
@@ -218,6 +223,7 @@ int demo_encode(const demo_cfg* cfg, uint64_t n_elems, const float* grad, float*
     a.beta = cfg->beta;
     a.k = slots_per_chunk(cfg);
     a.random = cfg->scheme == DEMO_SCHEME_RANDOM;
+    a.sign = (int)cfg->sign;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const unsigned grid = grid_for_groups(a.G);
     const bool wq = q_out != nullptr;
@@ -285,17 +291,29 @@ int demo_decode_apply(const demo_cfg* cfg, uint64_t n_elems, float* params, cons
     a.random = cfg->scheme == DEMO_SCHEME_RANDOM;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(grid_for_groups(a.G)), block(demo::kBlock);
-    if (cfg->scheme == DEMO_SCHEME_DCT) {
+    const uint64_t entries = (uint64_t)R * (uint64_t)a.k;  // payload entries per chunk
+    if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
         switch (cfg->value_fmt) {
         case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY>), grid, block, 0, s, a); break;
         case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16>), grid, block, 0, s, a); break;
         default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32>), grid, block, 0, s, a); break;
         }
+    } else if (cfg->scheme == DEMO_SCHEME_DCT) {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY>), grid, block, 0, s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32>), grid, block, 0, s, a); break;
+        }
     } else {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY>), grid, block, 0, s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32>), grid, block, 0, s, a); break;
+        case DEMO_VAL_TERNARY:
+            if (entries > kSelScalarEntries)
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false>), grid, block, 0, s, a);
+            break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false>), grid, block, 0, s, a); break;
         }
     }
     return launch_status();

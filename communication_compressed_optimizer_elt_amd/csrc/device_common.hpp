@@ -34,6 +34,17 @@ __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Workgroups are handed to the chip's 8 XCDs round-robin by id.  Renumber
+// them so that each XCD takes one contiguous run of ids (XCD x gets
+// ceil or floor of nb/8 of them): payload words that neighbouring groups share
+// in one cache line are then fetched by one L2 only.
+constexpr uint32_t kXcds = 8;
+__device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nb) {
+    const uint32_t x = b % kXcds, pos = b / kXcds;
+    const uint32_t q = nb / kXcds, rem = nb % kXcds;
+    return x * q + (x < rem ? x : rem) + pos;
+}
+
 __device__ __forceinline__ float sgnf(float x) {
     return x > 0.f ? 1.f : (x < 0.f ? -1.f : 0.f);
 }

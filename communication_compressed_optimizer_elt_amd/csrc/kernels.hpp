@@ -29,6 +29,7 @@ struct EncArgs {
     float beta;
     int k;
     int random;     // 1: positions from random_mask per chunk
+    int sign;       // 1: slots carry sign(value); 0: the value itself
 };
 
 struct DecArgs {
@@ -146,6 +147,19 @@ __device__ __forceinline__ void fill_basis_table(float* tab) {
 
 __device__ __forceinline__ uint16_t f16_of_sign(float v) {
     return v > 0.f ? (uint16_t)0x3C00u : (v < 0.f ? (uint16_t)0xBC00u : (uint16_t)0u);
+}
+
+// binary16 bits of v, rounded to nearest even (subnormals kept)
+__device__ __forceinline__ uint16_t f16_bits(float v) {
+    return __half_as_ushort(__float2half_rn(v));
+}
+
+// what a value-format slot carries: sign(v) or v itself
+__device__ __forceinline__ float wire_f32(float v, int sign) {
+    return sign ? sgnf(v) : v;
+}
+__device__ __forceinline__ uint16_t wire_f16(float v, int sign) {
+    return sign ? f16_of_sign(v) : f16_bits(v);
 }
 
 // ------------------------------------------------------------ encode (DCT) --
@@ -266,12 +280,12 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
                     float* val = reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k;
 #pragma unroll
                     for (int p = 0; p < KS; p++)
-                        if (p < k) val[p] = sgnf(selv[p]);
+                        if (p < k) val[p] = wire_f32(selv[p], a.sign);
                 } else if (VF == VF_F16) {
                     uint16_t* val = reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k;
 #pragma unroll
                     for (int p = 0; p < KS; p++)
-                        if (p < k) val[p] = f16_of_sign(selv[p]);
+                        if (p < k) val[p] = wire_f16(selv[p], a.sign);
                 }
             }
             if (VF == VF_TERNARY) {
@@ -322,9 +336,9 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
                     if (valid) {
                         idx[s] = (uint8_t)j;
                         if (VF == VF_F32)
-                            (reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = sgnf(X[j]);
+                            (reinterpret_cast<float*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = wire_f32(X[j], a.sign);
                         else if (VF == VF_F16)
-                            (reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = f16_of_sign(X[j]);
+                            (reinterpret_cast<uint16_t*>(a.pay + a.val_off) + c * (uint64_t)k)[s] = wire_f16(X[j], a.sign);
                     }
                     s++;
                 }
@@ -397,6 +411,23 @@ __device__ __forceinline__ void store_slot_values(uint8_t* val, uint64_t c, int 
     }
 }
 
+// Slot values of chunk c taken as they are (sign off): slot s is the s-th
+// set position of mask, read from the lane's row of the LDS tile holding u.
+template <int VF>
+__device__ __forceinline__ void store_slot_raw(uint8_t* val, uint64_t c, int k, const float* st, int lane,
+                                               uint32_t mask) {
+    uint32_t mm = mask;
+    for (int s = 0; s < k; s++) {
+        const uint32_t j = __builtin_ctz(mm) & 31u;  // mm keeps k set bits for k draws
+        mm &= mm - 1u;
+        const float x = st[swz(lane, (int)j)];
+        if (VF == VF_F32)
+            reinterpret_cast<float*>(val)[c * (uint64_t)k + s] = x;
+        else
+            reinterpret_cast<uint16_t*>(val)[c * (uint64_t)k + s] = f16_bits(x);
+    }
+}
+
 // ---------------------------------------- encode (Random / Striding / DiLoCo) --
 
 template <int VF, bool WQ>
@@ -458,7 +489,10 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
                 reinterpret_cast<uint64_t*>(a.pay + a.neg_off)[grp * (uint64_t)k + lane] = myneg;
             }
         } else if (valid) {
-            store_slot_values<VF>(a.pay + a.val_off, c, k, nzv, negv);
+            if (a.sign)
+                store_slot_values<VF>(a.pay + a.val_off, c, k, nzv, negv);
+            else
+                store_slot_raw<VF>(a.pay + a.val_off, c, k, st, lane, mask);
         }
 
         put_chunk(st, lane, mo);
@@ -607,9 +641,55 @@ __device__ __forceinline__ void apply_update(const DecArgs& a, const float* st, 
     }
 }
 
-// DCT scheme.  Few entries per chunk (R*k <= kSparseEntries): Q accumulated
-// directly from basis rows; otherwise the entries are summed per frequency in
-// LDS and Q is one full inverse transform.
+// Ternary words of many payload entries (entry e = r*k + s: replica r, slot
+// s of the wave's group) staged through LDS: each lane fetches whole words
+// with coalesced vector loads that all go out together, and stores them as
+// {nz.lo, neg.lo, nz.hi, neg.hi}, so that every lane then reads the halves
+// holding its own chunk's bits with one LDS read (two addresses per wave).
+struct WordStage {
+    int lr, ls, rpr;  // this lane's replica and slot within a round; replicas per round
+};
+
+__device__ __forceinline__ WordStage word_stage(int k, int lane) {
+    WordStage w;
+    w.rpr = kWave / k;
+    w.lr = lane / k;
+    w.ls = lane - w.lr * k;
+    return w;
+}
+
+// stage replicas [r0, r0 + nrep) of group grp, nrep <= ROUNDS * rpr
+template <int ROUNDS>
+__device__ __forceinline__ void stage_words(const DecArgs& a, uint64_t grp, uint4* ws, const WordStage& w, int r0,
+                                            int nrep) {
+    uint64_t nzv[ROUNDS], ngv[ROUNDS];
+#pragma unroll
+    for (int i = 0; i < ROUNDS; i++) {
+        const int r = r0 + i * w.rpr + w.lr;
+        const int rc = r < a.R ? r : a.R - 1;  // clamped: every address stays inside the payloads
+        const uint8_t* pr = a.pay + (uint64_t)rc * a.stride;
+        const uint64_t word = grp * (uint64_t)a.k + w.ls;
+        nzv[i] = reinterpret_cast<const uint64_t*>(pr + a.nz_off)[word];
+        ngv[i] = reinterpret_cast<const uint64_t*>(pr + a.neg_off)[word];
+    }
+#pragma unroll
+    for (int i = 0; i < ROUNDS; i++) {
+        const int rl = i * w.rpr + w.lr;
+        if (w.lr < w.rpr && rl < nrep)
+            ws[rl * a.k + w.ls] = make_uint4((uint32_t)nzv[i], (uint32_t)ngv[i], (uint32_t)(nzv[i] >> 32),
+                                             (uint32_t)(ngv[i] >> 32));
+    }
+}
+
+// this lane's ternary value of staged entry e, as an integer in {-1, 0, 1}
+__device__ __forceinline__ int staged_ternary(const uint4* ws, int e, int lane) {
+    const uint2 h = reinterpret_cast<const uint2*>(ws)[2 * e + (lane >> 5)];
+    const uint32_t sh = (uint32_t)lane & 31u;
+    return (int)((h.x >> sh) & 1u) - 2 * (int)((h.y >> sh) & 1u);  // NEG implies NZ
+}
+
+// DCT scheme, few entries per chunk (R*k <= kSparseEntries): Q accumulated
+// directly from basis rows of an LDS table.
 constexpr int kSparseEntries = 8;
 
 template <int VF>
@@ -617,87 +697,6 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     __shared__ float tab[kChunk * kTabStride];
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     fill_basis_table(tab);
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    float* st = stage_all + wv * kGroupElems;
-    const int k = a.k, R = a.R;
-    const bool sparse = (uint64_t)R * (uint64_t)k <= (uint64_t)kSparseEntries;
-
-    {
-        const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + wv;
-        if (grp >= a.G) return;
-        const uint64_t base = grp * kGroupElems;
-        const bool full = base + kGroupElems <= a.n;
-        const uint64_t c = grp * kWave + lane;
-        const bool valid = c < a.C;
-        const uint64_t cv = valid ? c : 0;
-
-        float Q[32];
-        wave_lds_sync();
-        if (sparse) {
-#pragma unroll
-            for (int i = 0; i < 32; i++) Q[i] = 0.f;
-            for (int r = 0; r < R; r++) {
-                const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
-                for (int s = 0; s < k; s++) {
-                    const int j = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
-                    const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
-                    const float* t = tab + j;
-#pragma unroll
-                    for (int i = 0; i < 32; i++) Q[i] = fmaf(v, t[i * kTabStride], Q[i]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; q++)
-                *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
-            // entries in batches of 8: all loads of a batch go out before its LDS adds
-            const int ne = R * k;
-            for (int e0 = 0; e0 < ne; e0 += 8) {
-                int jj[8];
-                float vv[8];
-#pragma unroll
-                for (int b = 0; b < 8; b++) {
-                    jj[b] = 0;
-                    vv[b] = 0.f;
-                    const int e = e0 + b;
-                    if (e < ne) {
-                        const int rr = e / k, s = e - rr * k;
-                        const uint8_t* pr = a.pay + (uint64_t)rr * a.stride;
-                        jj[b] = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
-                        if (VF == VF_TERNARY) {
-                            const uint64_t w = grp * (uint64_t)k + s;
-                            vv[b] = ternary_of(load_const_u64(pr + a.nz_off, w), load_const_u64(pr + a.neg_off, w),
-                                               lane);
-                        } else {
-                            vv[b] = slot_value<VF>(a, pr, grp, cv, s, lane);
-                        }
-                    }
-                }
-#pragma unroll
-                for (int b = 0; b < 8; b++)
-                    if (e0 + b < ne && valid) atomicAdd(st + swz(lane, jj[b]), vv[b]);
-            }
-            float A[32];
-            get_chunk(st, lane, A);
-            idct32(A, Q);
-        }
-#pragma unroll
-        for (int i = 0; i < 32; i++) Q[i] *= a.invR;
-        put_chunk(st, lane, Q);
-        wave_lds_sync();
-        apply_update(a, st, base, full, lane);
-    }
-}
-
-// Random / Striding / DiLoCo: every replica's slot s sits at the s-th selected
-// position, so the replicas are summed per slot in registers first (ternary
-// planes: wave-uniform 64-chunk words, scalar loads; value formats: the lane's
-// own k values), then each slot sum is written once to its position in the
-// lane's LDS tile and the tile updates theta in coalesced order.
-template <int VF>
-__global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
-    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
@@ -710,22 +709,170 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
     const uint64_t cv = valid ? c : 0;
+
+    float Q[32];
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < 32; i++) Q[i] = 0.f;
+    for (int r = 0; r < R; r++) {
+        const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+        for (int s = 0; s < k; s++) {
+            const int j = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
+            const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
+            const float* t = tab + j;
+#pragma unroll
+            for (int i = 0; i < 32; i++) Q[i] = fmaf(v, t[i * kTabStride], Q[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; i++) Q[i] *= a.invR;
+    put_chunk(st, lane, Q);
+    wave_lds_sync();
+    apply_update(a, st, base, full, lane);
+}
+
+// DCT scheme, many entries per chunk: the entries are summed per frequency in
+// the lane's row of the LDS tile (ternary sums are exact), Q is one full
+// inverse transform of that row.  A row belongs to one lane, so the sums are
+// plain LDS read-add-writes in program order (LDS float atomics measured 4x
+// slower here).  Entries go in batches of 16 whose index and value loads are
+// all issued before the batch's adds.
+constexpr int kDenseRounds = 2;  // words of up to 2*64 entries staged at a time
+constexpr int kDenseBatch = 16;
+
+template <int VF>
+__global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    __shared__ uint4 words_all[VF == VF_TERNARY ? kWavesPerBlock * kDenseRounds * kWave : 1];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float* st = stage_all + wv * kGroupElems;
+    uint4* ws = words_all + (VF == VF_TERNARY ? wv * kDenseRounds * kWave : 0);
+    const int k = a.k, R = a.R;
+
+    const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+    if (grp >= a.G) return;
+    const uint64_t base = grp * kGroupElems;
+    const bool full = base + kGroupElems <= a.n;
+    const uint64_t c = grp * kWave + lane;
+    const bool valid = c < a.C;
+    const uint64_t cv = valid ? c : 0;
+    const WordStage w = word_stage(k, lane);
+    const int pass = kDenseRounds * w.rpr;  // replicas per staging pass
+
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < 8; q++)
+        *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int r0 = 0; r0 < R; r0 += pass) {
+        const int nrep = R - r0 < pass ? R - r0 : pass;
+        const int ne = nrep * k;
+        if (VF == VF_TERNARY) {
+            wave_lds_sync();
+            stage_words<kDenseRounds>(a, grp, ws, w, r0, nrep);
+            wave_lds_sync();
+        }
+        int r = r0, s = 0;  // replica and slot of the next entry (wave-uniform)
+        for (int e0 = 0; e0 < ne; e0 += kDenseBatch) {
+            int jj[kDenseBatch];
+            float vv[kDenseBatch];
+#pragma unroll
+            for (int t = 0; t < kDenseBatch; t++) {
+                const bool live = e0 + t < ne;
+                // past the last entry r reaches r0 + nrep with s = 0: clamp the replica
+                const int rc = live ? r : r0 + nrep - 1;
+                const uint8_t* pr = a.pay + (uint64_t)rc * a.stride;
+                jj[t] = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
+                float v;
+                if (VF == VF_TERNARY)
+                    v = (float)staged_ternary(ws, live ? e0 + t : ne - 1, lane);
+                else
+                    v = slot_value<VF>(a, pr, grp, cv, s, lane);
+                vv[t] = (live && valid) ? v : 0.f;
+                if (++s == k) {
+                    s = 0;
+                    r++;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < kDenseBatch; t++)
+                if (e0 + t < ne) st[swz(lane, jj[t])] += vv[t];  // the row is this lane's alone
+        }
+    }
+    float A[32], Q[32];
+    wave_lds_sync();
+    get_chunk(st, lane, A);
+    idct32(A, Q);
+#pragma unroll
+    for (int i = 0; i < 32; i++) Q[i] *= a.invR;
+    put_chunk(st, lane, Q);
+    wave_lds_sync();
+    apply_update(a, st, base, full, lane);
+}
+
+// Random / Striding / DiLoCo: every replica's slot s sits at the s-th selected
+// position, so the replicas are summed per slot in registers first (value
+// formats: the lane's own k values; ternary planes: few entries as
+// wave-uniform scalar word loads, many entries (STAGED) through the word
+// stage), then each slot sum is written once to its position in the lane's
+// LDS tile and the tile updates theta in coalesced order.
+constexpr int kSelRounds = 8;  // the 8 KB tile holds the words of 8*64 entries
+
+template <int VF, bool STAGED>
+__global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
+    __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    float* st = stage_all + wv * kGroupElems;
+    const int k = a.k, R = a.R;
+
+    const uint32_t blk = STAGED ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint64_t grp = (uint64_t)blk * kWavesPerBlock + wv;
+    if (grp >= a.G) return;
+    const uint64_t base = grp * kGroupElems;
+    const bool full = base + kGroupElems <= a.n;
+    const uint64_t c = grp * kWave + lane;
+    const bool valid = c < a.C;
+    const uint64_t cv = valid ? c : 0;
     const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + cv, k) : a.mask;
 
     float A[32];
 #pragma unroll
     for (int s = 0; s < 32; s++) A[s] = 0.f;
-    for (int r = 0; r < R; r++) {
-        const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
-        if (VF == VF_TERNARY) {
+    if (VF == VF_TERNARY && STAGED) {
+        uint4* ws = reinterpret_cast<uint4*>(st);
+        const WordStage w = word_stage(k, lane);
+        const int pass = kSelRounds * w.rpr;
+        int T[32];
 #pragma unroll
-            for (int s = 0; s < 32; s++)
-                if (s < k) {
-                    const uint64_t w = grp * (uint64_t)k + s;
-                    A[s] += ternary_of(load_const_u64(pr + a.nz_off, w), load_const_u64(pr + a.neg_off, w), lane);
-                }
-        } else {
-            add_slot_values<VF>(pr + a.val_off, cv, k, A);
+        for (int s = 0; s < 32; s++) T[s] = 0;
+        for (int r0 = 0; r0 < R; r0 += pass) {
+            const int nrep = R - r0 < pass ? R - r0 : pass;
+            wave_lds_sync();
+            stage_words<kSelRounds>(a, grp, ws, w, r0, nrep);
+            wave_lds_sync();
+            for (int rl = 0; rl < nrep; rl++) {
+#pragma unroll
+                for (int s = 0; s < 32; s++)
+                    if (s < k) T[s] += staged_ternary(ws, rl * k + s, lane);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 32; s++) A[s] = (float)T[s];
+    } else {
+        for (int r = 0; r < R; r++) {
+            const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
+            if (VF == VF_TERNARY) {
+#pragma unroll
+                for (int s = 0; s < 32; s++)
+                    if (s < k) {
+                        const uint64_t wd = grp * (uint64_t)k + s;
+                        A[s] += ternary_of(load_const_u64(pr + a.nz_off, wd), load_const_u64(pr + a.neg_off, wd),
+                                           lane);
+                    }
+            } else {
+                add_slot_values<VF>(pr + a.val_off, cv, k, A);
+            }
         }
     }
 

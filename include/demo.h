@@ -69,7 +69,13 @@ typedef struct demo_cfg {
     uint32_t k;            /* DCT: top-k in [1,32]; RANDOM: n in [1,32];
                               STRIDE: n with 32 % n == 0; DILOCO: ignored (32) */
     uint32_t period;       /* DILOCO: sync when step % period == period-1; >= 1 */
-    uint32_t sign;         /* 1 = sign before sync.  Must be 1 in this build. */
+    uint32_t sign;         /* 1 = sign before sync: every slot carries sign(value)
+                              in {-1, 0, +1} ("Sign function" section).
+                              0 = slots carry the selected values themselves:
+                              the DCT coefficient (DCT) or u (others), stored
+                              as fp32 or as fp16 rounded to nearest even with
+                              subnormals kept; needs value_fmt F16 or F32
+                              (TERNARY with sign 0 is DEMO_EINVAL). */
     uint32_t value_fmt;    /* DEMO_VAL_* */
     uint32_t reserved;     /* must be 0 */
     float beta;            /* momentum decay, finite */
@@ -89,7 +95,8 @@ typedef struct demo_cfg {
  *   NZ   uint64 [G][k]  TERNARY: bit b of word g*k+s is set iff slot s of chunk
  *   NEG  uint64 [G][k]  64g+b is nonzero / negative.  Value = NZ ? (NEG ? -1 :
  *                       +1) : 0.  NEG without NZ and bits of chunks >= C are 0.
- *   VAL  fp16|fp32 [C][k] F16/F32: value of slot s of chunk c at entry c*k+s.
+ *   VAL  fp16|fp32 [C][k] F16/F32: value of slot s of chunk c at entry c*k+s:
+ *                       +-1 or 0 with sign 1, the value itself with sign 0.
  * RANDOM, STRIDE and DILOCO carry no IDX: every replica recomputes the slot
  * positions from (seed, step, chunk) and slots follow ascending position.
  */
@@ -117,8 +124,8 @@ int demo_payload_layout(const demo_cfg *cfg, uint64_t n_elems, demo_layout *out)
  *   coefficients|, equal magnitudes to the lower index; RANDOM / STRIDE: the
  *   shared positions; DILOCO: all 32 on a sync step, none otherwise);
  *   q = inverse DCT of the selected coefficients (DCT) or u on the selected
- *   positions (others); momentum <- u - q; payload <- ternary signs (and
- *   positions for DCT).
+ *   positions (others); momentum <- u - q; payload <- the slot values, as
+ *   ternary signs or (sign 0) the values themselves, and positions for DCT.
  * grad      [n_elems] read-only.
  * momentum  [n_elems] updated in place.
  * payload_out  >= demo_payload_layout(...).total_bytes bytes, 16-byte aligned.

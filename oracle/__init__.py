@@ -97,6 +97,8 @@ def lib():
         L.oracle_to_f16_bits.restype = ctypes.c_uint16
         L.oracle_from_f16_bits.argtypes = [ctypes.c_uint16]
         L.oracle_from_f16_bits.restype = ctypes.c_double
+        L.oracle_wire_value.argtypes = [ctypes.POINTER(_Params), ctypes.c_double]
+        L.oracle_wire_value.restype = ctypes.c_double
         L.oracle_encode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, P, P, P, P, P, P]
         L.oracle_encode.restype = ctypes.c_int
         L.oracle_decode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, ctypes.c_int32,
@@ -177,6 +179,13 @@ def to_f16_bits(x: float) -> int:
 
 def from_f16_bits(h: int) -> float:
     return float(lib().oracle_from_f16_bits(h))
+
+
+def wire_value(p: Params, x: float) -> float:
+    """The value a slot carries for the selected value x: sign(x) with the sign
+    on, else x rounded to the payload's fp16 or fp32 format."""
+    c = p.c()
+    return float(lib().oracle_wire_value(ctypes.byref(c), float(x)))
 
 
 def slots(p: Params) -> int:

@@ -324,7 +324,7 @@ static double sgn_of(double x)
 }
 
 /* the value a slot carries on the wire */
-static double wire_value(const oracle_params *p, double x)
+double oracle_wire_value(const oracle_params *p, double x)
 {
     if (p->sign)
         return sgn_of(x);
@@ -388,7 +388,7 @@ int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
                 Xs[j] = 0.0;
             for (int s = 0; s < slots; s++) {
                 Xs[sel[s]] = X[sel[s]];
-                val[s] = wire_value(p, X[sel[s]]);
+                val[s] = oracle_wire_value(p, X[sel[s]]);
             }
             idct_with(B, Xs, q);
         } else {
@@ -399,7 +399,7 @@ int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
                 if (mask & (1u << j)) {
                     q[j] = u[j];
                     sel[s] = j;
-                    val[s] = wire_value(p, u[j]);
+                    val[s] = oracle_wire_value(p, u[j]);
                     s++;
                 }
             }

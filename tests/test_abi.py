@@ -65,7 +65,7 @@ def _cfg(**kw):
     (dict(scheme=L.SCHEME_DILOCO, period=0), L.EINVAL),
     (dict(scheme=7), L.EINVAL),
     (dict(value_fmt=3), L.EINVAL),
-    (dict(sign=0), L.EUNSUPPORTED),
+    (dict(sign=0), L.EINVAL),  # ternary planes carry signs only
     (dict(sign=2), L.EINVAL),
     (dict(reserved=1), L.EINVAL),
     (dict(beta=float("nan")), L.EINVAL),

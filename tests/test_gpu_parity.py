@@ -14,7 +14,7 @@ import pytest
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 
-from harness import TOL, ParityRun  # noqa: E402
+from harness import TOL, ParityRun, oracle_params  # noqa: E402
 
 import oracle  # noqa: E402
 from communication_compressed_optimizer_elt_amd import binding as L  # noqa: E402
@@ -106,6 +106,52 @@ def test_stride_scheme(torch_cuda, fmt, k):
 def test_diloco_scheme(torch_cuda, fmt, period):
     cfg = L.Config(scheme=L.SCHEME_DILOCO, period=period, value_fmt=fmt)
     _run(torch_cuda, cfg, 32 * 64 * 2 + 3, 2, 17 if period == 16 else 6)
+
+
+@pytest.mark.parametrize("scheme,k,fmt,R", [
+    (L.SCHEME_DCT, 12, L.VAL_TERNARY, 17),   # 204 entries: two word-staging passes, 4 idle lanes
+    (L.SCHEME_DCT, 32, L.VAL_TERNARY, 5),    # 160 entries, two passes of 4 replicas
+    (L.SCHEME_DCT, 3, L.VAL_F16, 17),
+    (L.SCHEME_DCT, 1, L.VAL_TERNARY, 70),    # more replicas than one staging pass
+    (L.SCHEME_RANDOM, 32, L.VAL_TERNARY, 17),  # 544 entries: two passes of 16 replicas
+    (L.SCHEME_RANDOM, 3, L.VAL_TERNARY, 17),   # 51 entries, 21 replicas per round
+    (L.SCHEME_RANDOM, 8, L.VAL_F32, 17),
+    (L.SCHEME_STRIDE, 16, L.VAL_TERNARY, 5),
+    (L.SCHEME_DILOCO, 32, L.VAL_TERNARY, 17),
+])
+def test_many_replicas(torch_cuda, scheme, k, fmt, R):
+    """Decode of many payload entries per chunk (R*k large), all layouts of
+    the per-replica word staging."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, period=1, seed=11)
+    _run(torch_cuda, cfg, 32 * 64 * 5 + 33, R, 2)
+
+
+@pytest.mark.parametrize("scheme,k,fmt,R", [
+    (L.SCHEME_DCT, 1, L.VAL_F32, 2),
+    (L.SCHEME_DCT, 4, L.VAL_F16, 2),
+    (L.SCHEME_DCT, 12, L.VAL_F32, 2),    # any-k selection path
+    (L.SCHEME_DCT, 12, L.VAL_F16, 3),
+    (L.SCHEME_DCT, 2, L.VAL_F16, 9),     # many-entry decode
+    (L.SCHEME_RANDOM, 8, L.VAL_F16, 2),
+    (L.SCHEME_RANDOM, 16, L.VAL_F32, 2),
+    (L.SCHEME_STRIDE, 8, L.VAL_F16, 2),
+    (L.SCHEME_DILOCO, 32, L.VAL_F32, 2),
+])
+def test_sign_off_values(torch_cuda, scheme, k, fmt, R):
+    """Sign off: slots carry the coefficients (DCT) or u (others) as fp32 or
+    fp16, each replica decodes the values themselves."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=0, period=1, seed=3)
+    _run(torch_cuda, cfg, 32 * 64 * 3 + 17, R, 3)
+
+
+@pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 2), (L.SCHEME_RANDOM, 8)])
+def test_sign_off_fp16_subnormal_values(torch_cuda, scheme, k):
+    """|u| ~ 1e-6: the fp16 slot values fall in binary16's subnormal range."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=L.VAL_F16, sign=0)
+    run = _run(torch_cuda, cfg, 32 * 64 * 2 + 5, 2, 2, m_std=1e-6, g_std=1e-6)
+    idx, val, ok = oracle.unpack(oracle_params(cfg), run.n, run.pay[: run.stride].cpu().numpy())
+    assert ok
+    assert np.sum((np.abs(val) < 2.0 ** -14) & (val != 0)) > val.size // 2
 
 
 def test_zero_and_constant_chunks(torch_cuda):

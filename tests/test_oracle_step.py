@@ -121,6 +121,66 @@ def test_random_and_stride_select_the_shared_positions():
             assert np.array_equal(sh.m[c], expect_m)
 
 
+@pytest.mark.parametrize("fmt", [oracle.F32, oracle.F16])
+def test_sign_off_dct_carries_the_rounded_coefficients(fmt):
+    """Sign off: each slot carries the selected DCT coefficient itself, rounded
+    to the payload format (numpy's float32 / float16 conversions from fp64 are
+    round-to-nearest-even); selection and q are those of the signed run."""
+    L = 32 * 40
+    sh, m0, _ = _shard(L, seed=40)
+    g = _grad(L, seed=41)
+    p = Params(scheme=DCT, k=3, sign=0, value_fmt=fmt)
+    idx, val, q, _ = sh.encode(p, oracle.pad_chunks(g, L))
+    u = _u_ref(m0, g, 0.9, L)
+    Xref = scipy.fft.dct(u, type=2, norm="ortho", axis=1)
+    to = np.float32 if fmt == oracle.F32 else np.float16
+    for c in range(L // N):
+        sel = np.sort(np.argsort(-np.abs(Xref[c].astype(np.float32)), kind="stable")[:3])
+        assert np.array_equal(idx[c], sel)
+        assert np.array_equal(val[c], Xref[c][sel].astype(to).astype(np.float64))
+        Xs = np.zeros(N)
+        Xs[sel] = Xref[c][sel]
+        assert np.max(np.abs(q[c] - scipy.fft.idct(Xs, type=2, norm="ortho"))) < 1e-13
+
+
+@pytest.mark.parametrize("fmt", [oracle.F32, oracle.F16])
+def test_sign_off_random_carries_u_and_fp16_keeps_subnormals(fmt):
+    L = 32 * 30
+    sh, m0, _ = _shard(L, seed=42, m_std=1e-6)
+    g = (_grad(L, seed=43) * np.float32(1e-6)).astype(np.float32)  # |u| spans fp16's subnormal range
+    p = Params(scheme=RANDOM, k=8, seed=5, step=2, sign=0, value_fmt=fmt)
+    idx, val, _, _ = sh.encode(p, oracle.pad_chunks(g, L))
+    u = _u_ref(m0, g, 0.9, L)
+    to = np.float32 if fmt == oracle.F32 else np.float16
+    subnormal = 0
+    for c in range(L // N):
+        pos = [j for j in range(N) if (oracle.select_mask(5, 2, c, 8) >> j) & 1]
+        want = u[c][pos].astype(to)
+        assert np.array_equal(val[c], want.astype(np.float64))
+        subnormal += int(np.sum((np.abs(want) < 2.0 ** -14) & (want != 0)))
+    if fmt == oracle.F16:
+        assert subnormal > 100
+
+
+def test_decode_of_value_payloads_is_the_inverse_dct_of_the_mean():
+    C, k, R = 9, 5, 3
+    rng = np.random.default_rng(44)
+    pays = [_slots(C, k, rng) for _ in range(R)]
+    vals = [rng.standard_normal((C, k)) for _ in range(R)]
+    sh = Shard.contiguous(C * N, np.zeros(C * N, np.float32), rng.standard_normal(C * N).astype(np.float32))
+    th0 = sh.theta.copy()
+    p = Params(scheme=DCT, k=k, sign=0, value_fmt=oracle.F32, lr=1e-3)
+    Q = sh.decode(p, [i for i, _ in pays], vals)
+    for c in range(C):
+        A = np.zeros(N)
+        for r in range(R):
+            A[pays[r][0][c]] += vals[r][c]
+        Qref = scipy.fft.idct(A / R, type=2, norm="ortho")
+        assert np.max(np.abs(Q[c] - Qref)) < 1e-14
+        # theta ~ N(0, 1): a few units in the last place of fp64
+        assert np.max(np.abs(sh.theta[c] - (th0[c] - np.float64(np.float32(1e-3)) * Qref))) < 1e-15
+
+
 def test_ternary_values_and_sign_of_zero():
     L = 32 * 4
     sh = Shard.contiguous(L, np.zeros(L, np.float32), np.zeros(L, np.float32))
