@@ -546,11 +546,12 @@ __device__ __forceinline__ uint64_t load_const_u64(const uint8_t* base, uint64_t
     return ((const_u64_ptr)base)[word];
 }
 
-// k slot values of chunk c in a value-format payload (fp32 / fp16), added to A
+// k slot values of one chunk in a value-format payload (fp32 / fp16), added to
+// A; val points at the group's first entry, loff is the lane's entry offset
 template <int VF>
-__device__ __forceinline__ void add_slot_values(const uint8_t* val, uint64_t c, int k, float (&A)[32]) {
+__device__ __forceinline__ void add_slot_values(const uint8_t* val, uint32_t loff, int k, float (&A)[32]) {
     if (VF == VF_F32) {
-        const float* v = reinterpret_cast<const float*>(val) + c * (uint64_t)k;
+        const float* v = reinterpret_cast<const float*>(val) + loff;
         if ((k & 3) == 0) {
 #pragma unroll
             for (int s = 0; s < 32; s += 4)
@@ -567,7 +568,7 @@ __device__ __forceinline__ void add_slot_values(const uint8_t* val, uint64_t c, 
                 if (s < k) A[s] += v[s];
         }
     } else {
-        const uint16_t* v = reinterpret_cast<const uint16_t*>(val) + c * (uint64_t)k;
+        const uint16_t* v = reinterpret_cast<const uint16_t*>(val) + loff;
         if ((k & 7) == 0) {
 #pragma unroll
             for (int s = 0; s < 32; s += 8)
@@ -595,19 +596,32 @@ __device__ __forceinline__ float ternary_of(uint64_t nzw, uint64_t negw, int lan
     return nz ? (ng ? -1.f : 1.f) : 0.f;
 }
 
-// value of slot s of chunk c (lane) in replica payload pr
+// Per-chunk entries (IDX bytes, VAL values) of slot s in replica payload pr:
+// a wave-uniform base (replica, group, slot) plus the lane's own offset
+// loff = lane*k (0 for lanes past the last chunk), so the loads take a scalar
+// base and a 32-bit lane offset.
+__device__ __forceinline__ uint64_t group_entry(const DecArgs& a, uint64_t grp, int s) {
+    return grp * (uint64_t)(kWave * a.k) + (uint64_t)s;
+}
+
+__device__ __forceinline__ int slot_index(const DecArgs& a, const uint8_t* pr, uint64_t grp, int s, uint32_t loff) {
+    return (pr + a.idx_off + group_entry(a, grp, s))[loff] & 31;
+}
+
 template <int VF>
-__device__ __forceinline__ float slot_value(const DecArgs& a, const uint8_t* pr, uint64_t grp, uint64_t c, int s,
+__device__ __forceinline__ float slot_value(const DecArgs& a, const uint8_t* pr, uint64_t grp, int s, uint32_t loff,
                                             int lane) {
     if (VF == VF_TERNARY) {
+        // plain (vector) loads of the wave-uniform words: measured faster here
+        // than scalar loads, whose waits also cover the LDS table reads
         const uint64_t w = grp * (uint64_t)a.k + s;
-        const uint64_t nzw = reinterpret_cast<const uint64_t*>(pr + a.nz_off)[w];
-        const uint64_t negw = reinterpret_cast<const uint64_t*>(pr + a.neg_off)[w];
-        return ternary_of(nzw, negw, lane);
+        return ternary_of(reinterpret_cast<const uint64_t*>(pr + a.nz_off)[w],
+                          reinterpret_cast<const uint64_t*>(pr + a.neg_off)[w], lane);
     } else if (VF == VF_F32) {
-        return reinterpret_cast<const float*>(pr + a.val_off)[c * (uint64_t)a.k + s];
+        return (reinterpret_cast<const float*>(pr + a.val_off) + group_entry(a, grp, s))[loff];
     } else {
-        return __half2float(__ushort_as_half(reinterpret_cast<const uint16_t*>(pr + a.val_off)[c * (uint64_t)a.k + s]));
+        return __half2float(
+            __ushort_as_half((reinterpret_cast<const uint16_t*>(pr + a.val_off) + group_entry(a, grp, s))[loff]));
     }
 }
 
@@ -708,7 +722,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     const bool full = base + kGroupElems <= a.n;
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
-    const uint64_t cv = valid ? c : 0;
+    const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
 
     float Q[32];
     wave_lds_sync();
@@ -717,8 +731,8 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     for (int r = 0; r < R; r++) {
         const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
         for (int s = 0; s < k; s++) {
-            const int j = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
-            const float v = valid ? slot_value<VF>(a, pr, grp, cv, s, lane) : 0.f;
+            const int j = slot_index(a, pr, grp, s, loff);
+            const float v = valid ? slot_value<VF>(a, pr, grp, s, loff, lane) : 0.f;
             const float* t = tab + j;
 #pragma unroll
             for (int i = 0; i < 32; i++) Q[i] = fmaf(v, t[i * kTabStride], Q[i]);
@@ -756,9 +770,10 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     const bool full = base + kGroupElems <= a.n;
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
-    const uint64_t cv = valid ? c : 0;
+    const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
     const WordStage w = word_stage(k, lane);
     const int pass = kDenseRounds * w.rpr;  // replicas per staging pass
+    const int rowx = (lane & 7) << 2;       // swz(lane, j) = 32 lane + (j ^ rowx)
 
     wave_lds_sync();
 #pragma unroll
@@ -780,14 +795,15 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
             for (int t = 0; t < kDenseBatch; t++) {
                 const bool live = e0 + t < ne;
                 // past the last entry r reaches r0 + nrep with s = 0: clamp the replica
-                const int rc = live ? r : r0 + nrep - 1;
+                const int rc = __builtin_amdgcn_readfirstlane(live ? r : r0 + nrep - 1);
+                const int sc = __builtin_amdgcn_readfirstlane(s);
                 const uint8_t* pr = a.pay + (uint64_t)rc * a.stride;
-                jj[t] = pr[a.idx_off + cv * (uint64_t)k + s] & 31;
+                jj[t] = slot_index(a, pr, grp, sc, loff);
                 float v;
                 if (VF == VF_TERNARY)
                     v = (float)staged_ternary(ws, live ? e0 + t : ne - 1, lane);
                 else
-                    v = slot_value<VF>(a, pr, grp, cv, s, lane);
+                    v = slot_value<VF>(a, pr, grp, sc, loff, lane);
                 vv[t] = (live && valid) ? v : 0.f;
                 if (++s == k) {
                     s = 0;
@@ -796,7 +812,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
             }
 #pragma unroll
             for (int t = 0; t < kDenseBatch; t++)
-                if (e0 + t < ne) st[swz(lane, jj[t])] += vv[t];  // the row is this lane's alone
+                if (e0 + t < ne) st[lane * kChunk + (jj[t] ^ rowx)] += vv[t];  // the row is this lane's alone
         }
     }
     float A[32], Q[32];
@@ -810,13 +826,136 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     apply_update(a, st, base, full, lane);
 }
 
+// ---- bit-sliced counting of ternary planes over many replicas -------------
+//
+// For the position-aligned schemes every replica's slot s covers the same
+// chunk positions, so the decode needs, per chunk and slot, the number of set
+// NZ bits and set NEG bits over the R replicas (value = #NZ - 2 #NEG).  Lanes
+// count whole 32-bit plane halves (32 chunks per operation) into vertical
+// bit-plane counters: unit u = 2s + h (slot s, chunk half h) is shared by lpu
+// lanes, each adding every lpu-th replica with carry-save adders; a butterfly
+// over the unit's lanes adds their counters; the chunk lanes then read their
+// bit of each counter plane back from LDS.
+constexpr int kSelRounds = 8;  // the 8 KB tile holds the words of 8*64 entries
+constexpr int kCountPlanes = 8;  // counters up to 255 replicas
+constexpr int kMaxCountLanes = 8;
+constexpr int kCountMinR = 8;    // below it per-entry sums are cheaper (measured at R = 2)
+
+// (h, l) = a + b + c as a two-bit column sum, bitwise (carry-save adder)
+__device__ __forceinline__ void csa(uint32_t& h, uint32_t& l, uint32_t a, uint32_t b, uint32_t c) {
+    const uint32_t u = a ^ b;
+    h = (u & c) | (~u & a);
+    l = u ^ c;
+}
+
+// c += w[0] + ... + w[7], per bit position
+__device__ __forceinline__ void count8(uint32_t (&c)[kCountPlanes], const uint32_t (&w)[8]) {
+    uint32_t twosA, twosB, foursA, foursB, eights;
+    csa(twosA, c[0], c[0], w[0], w[1]);
+    csa(twosB, c[0], c[0], w[2], w[3]);
+    csa(foursA, c[1], c[1], twosA, twosB);
+    csa(twosA, c[0], c[0], w[4], w[5]);
+    csa(twosB, c[0], c[0], w[6], w[7]);
+    csa(foursB, c[1], c[1], twosA, twosB);
+    csa(eights, c[2], c[2], foursA, foursB);
+#pragma unroll
+    for (int b = 3; b < kCountPlanes; b++) {
+        const uint32_t t = c[b] & eights;
+        c[b] ^= eights;
+        eights = t;
+    }
+}
+
+// c += (counter of lane ^ d), per bit position
+__device__ __forceinline__ void add_partner(uint32_t (&c)[kCountPlanes], int d) {
+    uint32_t cy = 0;
+#pragma unroll
+    for (int b = 0; b < kCountPlanes; b++) {
+        const uint32_t o = (uint32_t)__shfl_xor((int)c[b], d);
+        const uint32_t t = c[b] ^ o;
+        const uint32_t sum = t ^ cy;
+        cy = (t & cy) | (~t & c[b]);
+        c[b] = sum;
+    }
+}
+
+// this lane's count (bit sh of every plane) from 8 planes in LDS
+__device__ __forceinline__ int read_count(const uint4* planes, uint32_t sh) {
+    const uint4 p0 = planes[0], p1 = planes[1];
+    const uint32_t w[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    uint32_t v = 0;
+#pragma unroll
+    for (int b = 0; b < kCountPlanes; b++) v |= ((w[b] >> sh) & 1u) << b;
+    return (int)v;
+}
+
+// T[s] = sum over the R replicas of slot s's ternary value for this lane's
+// chunk, R <= 255; st is the wave's 8 KB tile (staging, then counters)
+__device__ __forceinline__ void count_ternary(const DecArgs& a, uint64_t grp, float* st, int lane, int (&T)[32]) {
+    const int k = a.k, R = a.R;
+    uint4* ws = reinterpret_cast<uint4*>(st);
+    const WordStage w = word_stage(k, lane);
+    const int pass = kSelRounds * w.rpr;
+    const int units = 2 * k;
+    int lpu = 1;
+    while (lpu * 2 * units <= kWave && lpu * 2 <= kMaxCountLanes) lpu *= 2;
+    const int u = lane / lpu, j = lane - u * lpu;
+    const bool active = u < units;
+    const int us = active ? u >> 1 : 0, uh = active ? u & 1 : 0;
+
+    uint32_t cz[kCountPlanes], cn[kCountPlanes];
+#pragma unroll
+    for (int b = 0; b < kCountPlanes; b++) cz[b] = cn[b] = 0;
+    for (int r0 = 0; r0 < R; r0 += pass) {
+        const int nrep = R - r0 < pass ? R - r0 : pass;
+        wave_lds_sync();
+        stage_words<kSelRounds>(a, grp, ws, w, r0, nrep);
+        wave_lds_sync();
+        const uint2* ws2 = reinterpret_cast<const uint2*>(ws);
+        for (int i0 = 0; i0 * lpu < nrep; i0 += 8) {
+            uint32_t wz[8], wn[8];
+#pragma unroll
+            for (int t = 0; t < 8; t++) {
+                const int rl = j + (i0 + t) * lpu;
+                const bool live = active && rl < nrep;
+                const uint2 h = ws2[2 * ((live ? rl : 0) * k + us) + uh];
+                wz[t] = live ? h.x : 0u;
+                wn[t] = live ? h.y : 0u;
+            }
+            count8(cz, wz);
+            count8(cn, wn);
+        }
+    }
+    for (int d = 1; d < lpu; d *= 2) {
+        add_partner(cz, d);
+        add_partner(cn, d);
+    }
+    // counters to LDS: unit u's NZ planes at [4u, 4u+2), NEG planes at [4u+2, 4u+4)
+    wave_lds_sync();
+    if (active && j == 0) {
+        ws[4 * u + 0] = make_uint4(cz[0], cz[1], cz[2], cz[3]);
+        ws[4 * u + 1] = make_uint4(cz[4], cz[5], cz[6], cz[7]);
+        ws[4 * u + 2] = make_uint4(cn[0], cn[1], cn[2], cn[3]);
+        ws[4 * u + 3] = make_uint4(cn[4], cn[5], cn[6], cn[7]);
+    }
+    wave_lds_sync();
+    const uint32_t sh = (uint32_t)lane & 31u;
+    const int half = lane >> 5;
+#pragma unroll
+    for (int s = 0; s < 32; s++)
+        if (s < k) {
+            const uint4* pl = ws + 4 * (2 * s + half);
+            T[s] = read_count(pl, sh) - 2 * read_count(pl + 2, sh);
+        }
+}
+
 // Random / Striding / DiLoCo: every replica's slot s sits at the s-th selected
 // position, so the replicas are summed per slot in registers first (value
 // formats: the lane's own k values; ternary planes: few entries as
-// wave-uniform scalar word loads, many entries (STAGED) through the word
-// stage), then each slot sum is written once to its position in the lane's
-// LDS tile and the tile updates theta in coalesced order.
-constexpr int kSelRounds = 8;  // the 8 KB tile holds the words of 8*64 entries
+// wave-uniform scalar word loads; many entries (STAGED) through the word
+// stage, by bit-sliced counting from 8 replicas on), then each slot sum is
+// written once to its position in the lane's LDS tile and the tile updates
+// theta in coalesced order.
 
 template <int VF, bool STAGED>
 __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
@@ -834,12 +973,18 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
     const uint64_t cv = valid ? c : 0;
+    const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
     const uint32_t mask = a.random ? random_mask(a.seed, a.step_lo, a.chunk_offset + cv, k) : a.mask;
 
     float A[32];
 #pragma unroll
     for (int s = 0; s < 32; s++) A[s] = 0.f;
-    if (VF == VF_TERNARY && STAGED) {
+    if (VF == VF_TERNARY && STAGED && R >= kCountMinR && R < (1 << kCountPlanes)) {
+        int T[32];
+        count_ternary(a, grp, st, lane, T);
+#pragma unroll
+        for (int s = 0; s < 32; s++) A[s] = (float)T[s];
+    } else if (VF == VF_TERNARY && STAGED) {
         uint4* ws = reinterpret_cast<uint4*>(st);
         const WordStage w = word_stage(k, lane);
         const int pass = kSelRounds * w.rpr;
@@ -871,7 +1016,7 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
                                            lane);
                     }
             } else {
-                add_slot_values<VF>(pr + a.val_off, cv, k, A);
+                add_slot_values<VF>(pr + a.val_off + group_entry(a, grp, 0) * (VF == VF_F32 ? 4 : 2), loff, k, A);
             }
         }
     }

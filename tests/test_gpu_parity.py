@@ -118,6 +118,9 @@ def test_diloco_scheme(torch_cuda, fmt, period):
     (L.SCHEME_RANDOM, 8, L.VAL_F32, 17),
     (L.SCHEME_STRIDE, 16, L.VAL_TERNARY, 5),
     (L.SCHEME_DILOCO, 32, L.VAL_TERNARY, 17),
+    (L.SCHEME_RANDOM, 4, L.VAL_TERNARY, 255),  # largest R of the bit-sliced count
+    (L.SCHEME_RANDOM, 2, L.VAL_TERNARY, 256),  # beyond it: per-entry sums
+    (L.SCHEME_STRIDE, 1, L.VAL_TERNARY, 9),    # one slot, 8 lanes per unit
 ])
 def test_many_replicas(torch_cuda, scheme, k, fmt, R):
     """Decode of many payload entries per chunk (R*k large), all layouts of
