@@ -48,6 +48,7 @@ WORKLOADS = {
     "olmo2-1b-half-shard-decode-r64-demo-k1": ("olmo2", "dct", 1, "ternary", 64, "decode"),
     "olmo2-1b-half-shard-decode-r64-random-n8": ("olmo2", "random", 8, "ternary", 64, "decode"),
     "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
+    "olmo2-1b-full-demo-k1": ("olmo2-full", "dct", 1, "ternary", 2, "step"),
 }
 DILOCO_PERIOD = 16
 
@@ -93,7 +94,7 @@ def main() -> int:
     scheme = {"dct": L.SCHEME_DCT, "random": L.SCHEME_RANDOM, "stride": L.SCHEME_STRIDE,
               "diloco": L.SCHEME_DILOCO}[scheme_name]
     fmt = {"ternary": L.VAL_TERNARY, "f16": L.VAL_F16, "f32": L.VAL_F32}[fmt_name]
-    segs = synth.vit_b_set() if shard == "vit" else synth.olmo2_half_shard()
+    segs = {"vit": synth.vit_b_set, "olmo2": synth.olmo2_half_shard, "olmo2-full": synth.olmo2_full}[shard]()
     n = synth.shard_numel(segs)
     scales = synth.layer_scales(0, max(s.group for s in segs) + 1)
     g_std = 1e-2 if shard == "vit" else 1e-3

@@ -93,6 +93,14 @@ def olmo2_half_shard():
     return _segments(tensors, total // 2)
 
 
+def olmo2_full():
+    """Segments of the whole flattened OLMo2-1B-shaped model: the shard when
+    one data-parallel replica holds every parameter (shard group of size 1)."""
+    segs = _segments(olmo2_1b_tensors())
+    assert sum(s.numel for s in segs) == 1_279_395_840
+    return segs
+
+
 def vit_b_tensors():
     out = []
     for b in range(12):

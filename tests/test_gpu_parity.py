@@ -282,6 +282,14 @@ def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
     _run_full(torch_cuda, cfg, segs, 2, 3, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
 
 
+def test_olmo2_whole_model_on_one_shard(torch_cuda):
+    """The shard is the whole OLMo2-1B-shaped model (1,279,395,840 parameters,
+    one replica per shard group), DeMo k = 1, R = 2, sampled chunks."""
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    segs = synth.olmo2_full()
+    _run_full(torch_cuda, cfg, segs, 2, 3, 4999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
+
+
 def test_config4_olmo2_half_shard_diloco(torch_cuda):
     cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16)
     segs = synth.olmo2_half_shard()
