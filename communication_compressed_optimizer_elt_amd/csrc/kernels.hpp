@@ -791,20 +791,52 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
 // DCT scheme, many entries per chunk: the entries are summed per frequency in
 // the lane's row of the LDS tile, Q is one full inverse transform of that row.
 // A row belongs to one lane, so the sums are plain LDS read-add-writes in
-// program order (LDS float atomics measured 4x slower here); ternary entries
-// are summed as exact integers.  Entries go in batches of 16 whose index and
-// value loads are all issued before the batch's adds.
-constexpr int kDenseRounds = 2;  // words of up to 2*64 entries staged at a time
+// program order (LDS float atomics measured 4x slower here).
+//
+// Ternary payloads (R < 2^15): passes of up to 64 entries stage both the plane
+// words and the index bytes of the pass through LDS with coalesced vector
+// loads; each lane then reads its index byte and its two plane bits per entry
+// from LDS and adds NZ - 2 NEG into an int16 row (exact for R < 2^15).  The
+// tile's 8 KB hold the int16 rows (4 KB) and the staged index bytes (4 KB).
+// Value payloads (and ternary with more replicas): fp32 rows, entries in
+// batches of 16 whose index and value loads go out before the batch's adds.
 constexpr int kDenseBatch = 16;
+constexpr int kRowBytes = kWave * kChunk * 2;  // int16 rows of one wave
+
+// index bytes of replicas [r0, r0 + nrep) of group grp (nrep*k <= 64) into
+// is[rl*64k + c*k + s], by 16-byte units; units past the region's entries
+// (the last group) are skipped
+__device__ __forceinline__ void stage_index(const DecArgs& a, uint64_t grp, uint8_t* is, int r0, int nrep,
+                                            int lane) {
+    const int k = a.k;
+    const int upr = 4 * k;  // 16-byte units per replica row of 64k bytes
+    const uint64_t g0 = grp * (uint64_t)(kWave * k);
+    const uint64_t lim = a.C * (uint64_t)k;
+    const int units = nrep * upr;  // <= 256
+    uint4 v[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int u = lane + i * kWave;
+        const int rl = u / upr, off = (u - rl * upr) * 16;
+        ok[i] = u < units && g0 + off < lim;
+        const int rc = ok[i] ? r0 + rl : r0;
+        const uint64_t oc = ok[i] ? (uint64_t)off : 0;
+        v[i] = *reinterpret_cast<const uint4*>(a.pay + (uint64_t)rc * a.stride + a.idx_off + g0 + oc);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        if (ok[i]) *reinterpret_cast<uint4*>(is + (lane + i * kWave) * 16) = v[i];
+}
 
 template <int VF>
 __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
-    __shared__ uint4 words_all[VF == VF_TERNARY ? kWavesPerBlock * kDenseRounds * kWave : 1];
+    __shared__ uint4 words_all[VF == VF_TERNARY ? kWavesPerBlock * kWave : 1];
     const int lane = threadIdx.x & (kWave - 1);
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     float* st = stage_all + wv * kGroupElems;
-    uint4* ws = words_all + (VF == VF_TERNARY ? wv * kDenseRounds * kWave : 0);
+    uint4* ws = words_all + (VF == VF_TERNARY ? wv * kWave : 0);
     const int k = a.k, R = a.R;
 
     const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
@@ -816,64 +848,71 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
     const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
-    const WordStage w = word_stage(k, lane);
-    const int pass = kDenseRounds * w.rpr;  // replicas per staging pass
-    const int rowx = (lane & 7) << 2;       // swz(lane, j) = 32 lane + (j ^ rowx)
+    const int rowx = (lane & 7) << 2;  // swz(lane, j) = 32 lane + (j ^ rowx)
 
+    float A[32], Q[32];
     wave_lds_sync();
+    if (VF == VF_TERNARY && R < (1 << 15)) {
+        int16_t* row = reinterpret_cast<int16_t*>(st) + lane * kChunk;
+        uint8_t* is = reinterpret_cast<uint8_t*>(st) + kRowBytes;
 #pragma unroll
-    for (int q = 0; q < 8; q++)
-        *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int r0 = 0; r0 < R; r0 += pass) {
-        const int nrep = R - r0 < pass ? R - r0 : pass;
-        const int ne = nrep * k;
-        if (VF == VF_TERNARY) {
+        for (int q = 0; q < 4; q++) reinterpret_cast<uint4*>(row)[q] = make_uint4(0u, 0u, 0u, 0u);
+        const WordStage w = word_stage(k, lane);
+        const int pass = w.rpr;  // replicas per pass: rpr*k <= 64 entries
+        const uint2* ws2 = reinterpret_cast<const uint2*>(ws) + (lane >> 5);
+        const uint32_t sh = (uint32_t)lane & 31u;
+        const int rowstep = kWave * k - k;  // index-byte offset step when the slot wraps
+        for (int r0 = 0; r0 < R; r0 += pass) {
+            const int nrep = R - r0 < pass ? R - r0 : pass;
+            const int ne = nrep * k;
             wave_lds_sync();
-            stage_words<kDenseRounds>(a, grp, ws, w, r0, nrep);
+            stage_words<1>(a, grp, ws, w, r0, nrep);
+            stage_index(a, grp, is, r0, nrep, lane);
             wave_lds_sync();
-        }
-        if (VF == VF_TERNARY) {
-            // IDX of the next entry: pi[s][loff], replica advancing every k slots
-            const uint8_t* pi = a.pay + (uint64_t)r0 * a.stride + a.idx_off + group_entry(a, grp, 0);
-            int s = 0;
-            int* sti = reinterpret_cast<int*>(st) + lane * kChunk;
-            const uint2* ws2 = reinterpret_cast<const uint2*>(ws) + (lane >> 5);
-            const uint32_t sh = (uint32_t)lane & 31u;
+            const uint8_t* il = is + lane * k;  // entry (rl, s) at il[rl*64k + s]
+            int off = 0, s = 0;
             const int nfull = ne - ne % kDenseBatch;
             for (int e0 = 0; e0 < nfull; e0 += kDenseBatch) {
                 int jj[kDenseBatch], vi[kDenseBatch];
 #pragma unroll
                 for (int t = 0; t < kDenseBatch; t++) {
-                    jj[t] = pi[s + loff] & 31;
-                    const uint2 h = ws2[2 * (e0 + t)];
-                    vi[t] = lane_ternary(h, sh);
+                    jj[t] = il[off] & 31;
+                    vi[t] = lane_ternary(ws2[2 * (e0 + t)], sh);
+                    off++;
                     if (++s == k) {
                         s = 0;
-                        pi += a.stride;
+                        off += rowstep;
                     }
                 }
 #pragma unroll
-                for (int t = 0; t < kDenseBatch; t++) sti[jj[t] ^ rowx] += vi[t];
+                for (int t = 0; t < kDenseBatch; t++) row[jj[t] ^ rowx] += (int16_t)vi[t];
             }
             for (int e = nfull; e < ne; e++) {
-                const uint2 h = ws2[2 * e];
-                sti[(pi[s + loff] & 31) ^ rowx] += lane_ternary(h, sh);
+                row[(il[off] & 31) ^ rowx] += (int16_t)lane_ternary(ws2[2 * e], sh);
+                off++;
                 if (++s == k) {
                     s = 0;
-                    pi += a.stride;
+                    off += rowstep;
                 }
             }
-            continue;
         }
-        int r = r0, s = 0;  // replica and slot of the next entry (wave-uniform)
+        wave_lds_sync();
+#pragma unroll
+        for (int i = 0; i < 32; i++) A[i] = (float)row[i ^ rowx];
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; q++)
+            *reinterpret_cast<float4*>(st + swz(lane, 4 * q)) = make_float4(0.f, 0.f, 0.f, 0.f);
+        int r = 0, s = 0;  // replica and slot of the next entry (wave-uniform)
+        const int ne = R * k;
         for (int e0 = 0; e0 < ne; e0 += kDenseBatch) {
             int jj[kDenseBatch];
             float vv[kDenseBatch];
 #pragma unroll
             for (int t = 0; t < kDenseBatch; t++) {
                 const bool live = e0 + t < ne;
-                // past the last entry r reaches r0 + nrep with s = 0: clamp the replica
-                const int rc = __builtin_amdgcn_readfirstlane(live ? r : r0 + nrep - 1);
+                // past the last entry r reaches R with s = 0: clamp the replica
+                const int rc = __builtin_amdgcn_readfirstlane(live ? r : R - 1);
                 const int sc = __builtin_amdgcn_readfirstlane(s);
                 const uint8_t* pr = a.pay + (uint64_t)rc * a.stride;
                 jj[t] = slot_index(a, pr, grp, sc, loff);
@@ -888,17 +927,13 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
             for (int t = 0; t < kDenseBatch; t++)
                 if (e0 + t < ne) st[lane * kChunk + (jj[t] ^ rowx)] += vv[t];  // the row is this lane's alone
         }
-    }
-    float A[32], Q[32];
-    wave_lds_sync();
-    get_chunk(st, lane, A);
-    if (VF == VF_TERNARY) {  // the rows hold integer sums
-#pragma unroll
-        for (int i = 0; i < 32; i++) A[i] = (float)__float_as_int(A[i]);
+        wave_lds_sync();
+        get_chunk(st, lane, A);
     }
     idct32(A, Q);
 #pragma unroll
     for (int i = 0; i < 32; i++) Q[i] *= a.invR;
+    wave_lds_sync();
     put_chunk(st, lane, Q);
     wave_lds_sync();
     apply_update_prefetched(a, st, base, full, lane, th);
