@@ -134,3 +134,21 @@ def test_layout_agrees_with_the_oracle_codec(lib, scheme, k, fmt, n):
     got = L.demo_payload_layout(cfg, n)
     ref = oracle.payload_regions(oracle.Params(scheme=scheme, k=k, value_fmt=fmt), n)
     assert got == ref
+
+
+def test_plain_c_client(lib, tmp_path):
+    """tests/abi_from_c.c, a C99 program that includes only include/demo.h,
+    builds against the library with gcc and agrees with the oracle's layout."""
+    import subprocess
+
+    exe = tmp_path / "abi_from_c"
+    libdir = os.path.dirname(L.LIB_PATH)
+    subprocess.check_call(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                           os.path.join(ROOT, "tests", "abi_from_c.c"), "-o", str(exe),
+                           "-L", libdir, "-l:libdemo.so", f"-Wl,-rpath,{libdir}"])
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    got = {k: int(v) for k, v in (line.split() for line in out.stdout.strip().splitlines())}
+    ref = oracle.payload_regions(oracle.Params(scheme=oracle.DCT, k=1), 639697920)
+    for key in ("idx_off", "idx_bytes", "nz_off", "neg_off", "plane_bytes", "val_off", "val_bytes"):
+        assert got[key] == ref[key], key
