@@ -70,6 +70,23 @@ class Params:
                        self.beta, self.lr, self.seed, self.step)
 
 
+class _AdamW(ctypes.Structure):
+    _fields_ = [("beta2", ctypes.c_float), ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("reserved", ctypes.c_int32)]
+
+
+@dataclass
+class AdamW:
+    """Decoupled AdamW's extra knobs (beta1 is Params.beta)."""
+
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+    def c(self) -> _AdamW:
+        return _AdamW(self.beta2, self.eps, self.weight_decay, 0)
+
+
 _lib = None
 
 
@@ -104,6 +121,12 @@ def lib():
         L.oracle_decode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, ctypes.c_int32,
                                     P, P, P, P]
         L.oracle_decode.restype = ctypes.c_int
+        L.oracle_encode_adamw.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_AdamW), ctypes.c_int64,
+                                          P, P, P, P, P, P, P, P, P]
+        L.oracle_encode_adamw.restype = ctypes.c_int
+        L.oracle_decode_adamw.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_AdamW), ctypes.c_int64,
+                                          P, P, ctypes.c_int32, P, P, P, P, P]
+        L.oracle_decode_adamw.restype = ctypes.c_int
         L.oracle_payload_regions.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P]
         L.oracle_pack.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P, P, P]
         L.oracle_pack.restype = ctypes.c_int
@@ -198,22 +221,27 @@ def slots(p: Params) -> int:
 # --------------------------------------------------------------------------- #
 
 class Shard:
-    """fp64 state (m, theta) of a list of chunks of one shard.
+    """fp64 state (m, theta, and Decoupled AdamW's second moment v) of a list
+    of chunks of one shard.
 
     chunk_ids: global chunk index of each chunk (used by Random hashing).
     nvalid:    valid elements per chunk (32 except a ragged last chunk).
-    m0, theta0: fp32 inputs, [n][32] (padded positions ignored), widened to fp64.
+    m0, theta0, v0: fp32 inputs, [n][32] (padded positions ignored), widened
+    to fp64; v0 defaults to zeros.
     """
 
-    def __init__(self, chunk_ids, nvalid, m0, theta0):
+    def __init__(self, chunk_ids, nvalid, m0, theta0, v0=None):
         self.chunk_ids = np.ascontiguousarray(chunk_ids, np.uint64)
         self.nvalid = np.ascontiguousarray(nvalid, np.int32)
         n = len(self.chunk_ids)
         self.m = np.ascontiguousarray(np.asarray(m0, np.float32).reshape(n, CHUNK), np.float64)
         self.theta = np.ascontiguousarray(np.asarray(theta0, np.float32).reshape(n, CHUNK), np.float64)
+        self.v = (np.zeros((n, CHUNK), np.float64) if v0 is None else
+                  np.ascontiguousarray(np.asarray(v0, np.float32).reshape(n, CHUNK), np.float64))
         pad = np.arange(CHUNK)[None, :] >= self.nvalid[:, None]
         self.m[pad] = 0.0
         self.theta[pad] = 0.0
+        self.v[pad] = 0.0
 
     @classmethod
     def contiguous(cls, n_elems: int, m0_flat, theta0_flat, chunk_offset: int = 0):
@@ -227,8 +255,9 @@ class Shard:
     def n(self) -> int:
         return len(self.chunk_ids)
 
-    def encode(self, p: Params, g):
-        """Algorithm 1 steps 3-5. g is fp32 [n][32]. Returns (idx, val, q, X)."""
+    def encode(self, p: Params, g, adamw: AdamW | None = None):
+        """Algorithm 1 steps 3-5 (Decoupled AdamW's moments when adamw is
+        given). g is fp32 [n][32]. Returns (idx, val, q, X)."""
         n = self.n
         g = np.ascontiguousarray(np.asarray(g, np.float32).reshape(n, CHUNK))
         s = slots(p)
@@ -237,14 +266,21 @@ class Shard:
         q = np.zeros((n, CHUNK), np.float64)
         X = np.zeros((n, CHUNK), np.float64)
         c = p.c()
-        r = lib().oracle_encode(ctypes.byref(c), n, _ptr(self.chunk_ids), _ptr(self.nvalid), _ptr(g),
-                                _ptr(self.m), _ptr(idx), _ptr(val), _ptr(q), _ptr(X))
+        if adamw is None:
+            r = lib().oracle_encode(ctypes.byref(c), n, _ptr(self.chunk_ids), _ptr(self.nvalid), _ptr(g),
+                                    _ptr(self.m), _ptr(idx), _ptr(val), _ptr(q), _ptr(X))
+        else:
+            w = adamw.c()
+            r = lib().oracle_encode_adamw(ctypes.byref(c), ctypes.byref(w), n, _ptr(self.chunk_ids),
+                                          _ptr(self.nvalid), _ptr(g), _ptr(self.m), _ptr(self.v), _ptr(idx),
+                                          _ptr(val), _ptr(q), _ptr(X))
         if r < 0:
             raise ValueError("oracle_encode: bad configuration")
         return idx[:, :s], val[:, :s], q, X
 
-    def decode(self, p: Params, idx_list, val_list):
-        """Algorithm 1 steps 6-7 over R payloads (own first). Returns Q [n][32]."""
+    def decode(self, p: Params, idx_list, val_list, adamw: AdamW | None = None):
+        """Algorithm 1 steps 6-7 over R payloads (own first); with adamw the
+        update uses this shard's second moment. Returns Q [n][32]."""
         n = self.n
         R = len(val_list)
         s = slots(p)
@@ -256,8 +292,15 @@ class Shard:
             np.zeros((R, n, 1), np.float64))
         Q = np.zeros((n, CHUNK), np.float64)
         c = p.c()
-        if lib().oracle_decode(ctypes.byref(c), n, _ptr(self.chunk_ids), _ptr(self.nvalid), R,
-                               _ptr(idx), _ptr(val), _ptr(self.theta), _ptr(Q)) != 0:
+        if adamw is None:
+            rc = lib().oracle_decode(ctypes.byref(c), n, _ptr(self.chunk_ids), _ptr(self.nvalid), R,
+                                     _ptr(idx), _ptr(val), _ptr(self.theta), _ptr(Q))
+        else:
+            w = adamw.c()
+            rc = lib().oracle_decode_adamw(ctypes.byref(c), ctypes.byref(w), n, _ptr(self.chunk_ids),
+                                           _ptr(self.nvalid), R, _ptr(idx), _ptr(val), _ptr(self.v),
+                                           _ptr(self.theta), _ptr(Q))
+        if rc != 0:
             raise ValueError("oracle_decode: bad arguments")
         return Q
 

@@ -20,6 +20,9 @@
  *  - "DeMo: Decoupled Momentum Optimization" abstract: fast orthonormal
  *    transform (DCT) + top-k sparsification, momentum subtraction as error
  *    feedback.
+ *  - same notes, "Decoupled AdamW": an AdamW variant whose first and second
+ *    moments (the EMAs of the gradient and of its square) are not
+ *    synchronised.
  *
  * Readings where the pages are silent (each also listed in the design notes):
  *  - Delta is the plain gradient; eta appears only in the parameter update.
@@ -40,6 +43,12 @@
  *    q = u (all 32 positions).  Random/Striding/DiLoCo work in the parameter
  *    domain (no transform).
  *  - beta and eta are the fp32 configuration values widened to fp64.
+ *  - Decoupled AdamW (the notes give no formula): both moments are local and
+ *    never exchanged; the first moment m = beta1*m + (1-beta1)*g takes the
+ *    momentum's place in extraction and error feedback; v = beta2*v +
+ *    (1-beta2)*g^2; the exchanged Q is applied as AdamW applies its first
+ *    moment: theta -= eta*((Q/(1-beta1^t)) / (sqrt(v/(1-beta2^t)) + eps)
+ *    + wd*theta), t = step + 1.
  */
 #include <math.h>
 #include <omp.h>
@@ -64,6 +73,14 @@ typedef struct oracle_params {
     uint64_t seed;
     uint64_t step;
 } oracle_params;
+
+/* Decoupled AdamW's extra hyper-parameters (beta1 is oracle_params.beta). */
+typedef struct oracle_adamw {
+    float beta2;
+    float eps;
+    float weight_decay;
+    int32_t reserved;
+} oracle_adamw;
 
 /* threads the OpenMP loops below run on */
 int oracle_threads(void) { return omp_get_max_threads(); }
@@ -347,9 +364,9 @@ double oracle_wire_value(const oracle_params *p, double x)
 /* Returns slots per chunk, or -1 on a bad configuration.                    */
 /* ------------------------------------------------------------------------ */
 
-int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, const int32_t *nvalid,
-                  const float *g, double *m, int32_t *slot_idx, double *slot_val, double *q_out,
-                  double *x_out)
+static int encode_impl(const oracle_params *p, double gamma, int64_t n, const uint64_t *chunk_id,
+                       const int32_t *nvalid, const float *g, double *m, int32_t *slot_idx, double *slot_val,
+                       double *q_out, double *x_out)
 {
     if (p->scheme < OR_DCT || p->scheme > OR_DILOCO)
         return -1;
@@ -373,9 +390,10 @@ int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
         int32_t sel[OR_CHUNK];
         double val[OR_CHUNK];
 
-        /* step 3: momentum accumulation (pads are zero) */
+        /* step 3: momentum accumulation (pads are zero); gamma = 1, or 1 - beta1
+         * for the AdamW first moment */
         for (int i = 0; i < OR_CHUNK; i++)
-            u[i] = (i < nv) ? beta * mc[i] + (double)gc[i] : 0.0;
+            u[i] = (i < nv) ? beta * mc[i] + gamma * (double)gc[i] : 0.0;
 
         /* step 4: extract q */
         for (int i = 0; i < OR_CHUNK; i++)
@@ -425,6 +443,29 @@ int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
     return slots;
 }
 
+int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, const int32_t *nvalid,
+                  const float *g, double *m, int32_t *slot_idx, double *slot_val, double *q_out,
+                  double *x_out)
+{
+    return encode_impl(p, 1.0, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out);
+}
+
+/* Decoupled AdamW encode: the second moment v (fp64, [n][32], pads kept 0)
+ * takes g^2; the first moment m then goes through the same steps 3-5. */
+int oracle_encode_adamw(const oracle_params *p, const oracle_adamw *w, int64_t n, const uint64_t *chunk_id,
+                        const int32_t *nvalid, const float *g, double *m, double *v, int32_t *slot_idx,
+                        double *slot_val, double *q_out, double *x_out)
+{
+    const double beta2 = (double)w->beta2;
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < n; c++)
+        for (int i = 0; i < OR_CHUNK; i++) {
+            const double gi = (double)g[c * OR_CHUNK + i];
+            v[c * OR_CHUNK + i] = (i < nvalid[c]) ? beta2 * v[c * OR_CHUNK + i] + (1.0 - beta2) * gi * gi : 0.0;
+        }
+    return encode_impl(p, 1.0 - (double)p->beta, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Decode: Algorithm 1 steps 6-7 for a list of chunks.                       */
 /*   R payloads, each given as slot_idx [R][n][slots] (DCT only; the other   */
@@ -433,13 +474,22 @@ int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
 /*   Q_out (may be NULL) receives the aggregate Q, [n][32].                  */
 /* ------------------------------------------------------------------------ */
 
-int oracle_decode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, const int32_t *nvalid,
-                  int32_t R, const int32_t *slot_idx, const double *slot_val, double *theta,
-                  double *Q_out)
+static int decode_impl(const oracle_params *p, const oracle_adamw *w, const double *v, int64_t n,
+                       const uint64_t *chunk_id, const int32_t *nvalid, int32_t R, const int32_t *slot_idx,
+                       const double *slot_val, double *theta, double *Q_out)
 {
     if (R < 1)
         return -1;
+    /* AdamW: bias corrections of step t = step + 1 */
+    const double t = (double)p->step + 1.0;
+    const double c1 = w ? 1.0 / (1.0 - pow((double)p->beta, t)) : 1.0;
+    const double c2 = w ? 1.0 / (1.0 - pow((double)w->beta2, t)) : 1.0;
     const int slots = oracle_slots(p);
+    if (slots == 0) { /* DiLoCo between syncs: no payload, no update */
+        if (Q_out)
+            memset(Q_out, 0, sizeof(double) * (size_t)n * OR_CHUNK);
+        return 0;
+    }
     const double lr = (double)p->lr;
     double B[OR_CHUNK * OR_CHUNK];
     oracle_basis(B);
@@ -473,13 +523,34 @@ int oracle_decode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, c
                 }
             }
         }
-        for (int i = 0; i < nv; i++)
-            theta[c * OR_CHUNK + i] -= lr * Q[i];
+        for (int i = 0; i < nv; i++) {
+            double *th = &theta[c * OR_CHUNK + i];
+            if (w)
+                *th -= lr * (c1 * Q[i] / (sqrt(c2 * v[c * OR_CHUNK + i]) + (double)w->eps) +
+                             (double)w->weight_decay * *th);
+            else
+                *th -= lr * Q[i];
+        }
         if (Q_out)
             for (int i = 0; i < OR_CHUNK; i++)
                 Q_out[c * OR_CHUNK + i] = (i < nv) ? Q[i] : 0.0;
     }
     return 0;
+}
+
+int oracle_decode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, const int32_t *nvalid,
+                  int32_t R, const int32_t *slot_idx, const double *slot_val, double *theta,
+                  double *Q_out)
+{
+    return decode_impl(p, NULL, NULL, n, chunk_id, nvalid, R, slot_idx, slot_val, theta, Q_out);
+}
+
+/* Decoupled AdamW decode: Q as above, applied with the own second moment v. */
+int oracle_decode_adamw(const oracle_params *p, const oracle_adamw *w, int64_t n, const uint64_t *chunk_id,
+                        const int32_t *nvalid, int32_t R, const int32_t *slot_idx, const double *slot_val,
+                        const double *v, double *theta, double *Q_out)
+{
+    return decode_impl(p, w, v, n, chunk_id, nvalid, R, slot_idx, slot_val, theta, Q_out);
 }
 
 /* ------------------------------------------------------------------------ */
