@@ -49,7 +49,10 @@ WORKLOADS = {
     "olmo2-1b-half-shard-decode-r64-random-n8": ("olmo2", "random", 8, "ternary", 64, "decode"),
     "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
     "olmo2-1b-full-demo-k1": ("olmo2-full", "dct", 1, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-adamw-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
 }
+# Decoupled AdamW workloads: second moment v read and written by the encode, read by the decode
+ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1"}
 DILOCO_PERIOD = 16
 
 
@@ -108,9 +111,12 @@ def main() -> int:
     def sends(t):
         return scheme != L.SCHEME_DILOCO or t % DILOCO_PERIOD == DILOCO_PERIOD - 1
 
+    adamw = L.AdamW() if args.workload in ADAMW else None
+
     # ---- inputs, resident in HBM -------------------------------------------
     g = synth.scaled_grad_torch(segs, scales, g_std, 0, 0)
     m = torch.zeros(n, dtype=torch.float32, device=dev)
+    v = torch.zeros(n, dtype=torch.float32, device=dev) if adamw else None
     theta = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
     pay = torch.zeros(R * stride, dtype=torch.uint8, device=dev)
     # the other replicas' payloads: the encode of states drawn from their own
@@ -160,11 +166,19 @@ def main() -> int:
         # decode-only workloads decode the step-0 payloads (Random positions of step 0)
         dcfg = cfg if mode == "step" else L.Config(**{**cfg.__dict__, "step": 0})
         if mode == "step":
-            enc_bytes = 12 * n + (payload_bytes if sends(t) else 0)
-            timed("encode", enc_bytes, lambda: L.demo_encode(cfg, n, g, m, pay, None, stream), record)
+            enc_bytes = (20 if adamw else 12) * n + (payload_bytes if sends(t) else 0)
+            if adamw:
+                timed("encode", enc_bytes, lambda: L.demo_encode_adamw(cfg, adamw, n, g, m, v, pay, None, stream),
+                      record)
+            else:
+                timed("encode", enc_bytes, lambda: L.demo_encode(cfg, n, g, m, pay, None, stream), record)
         if sends(t):
-            timed("decode", 8 * n + R * payload_bytes,
-                  lambda: L.demo_decode_apply(dcfg, n, theta, pay, stride, R, stream), record)
+            if adamw:
+                timed("decode", 12 * n + R * payload_bytes,
+                      lambda: L.demo_decode_apply_adamw(dcfg, adamw, n, theta, v, pay, stride, R, stream), record)
+            else:
+                timed("decode", 8 * n + R * payload_bytes,
+                      lambda: L.demo_decode_apply(dcfg, n, theta, pay, stride, R, stream), record)
 
     for t in range(args.warmup):
         step(t, False)
@@ -209,7 +223,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n_elems": n, "scheme": scheme_name, "k": k,
+        "config": {"workload": args.workload, "n_elems": n, "optimizer": "decoupled-adamw" if adamw else "demo-sgd",
+                   "scheme": scheme_name, "k": k,
                    "value_fmt": fmt_name, "replicas": R, "chunk": 32, "mode": mode},
         "hbm_gbps": step_gbps,
         "pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
@@ -220,7 +235,7 @@ def main() -> int:
         "cpu_baseline": None,
     }
 
-    if not args.no_cpu_baseline and mode == "step" and scheme != L.SCHEME_DILOCO:
+    if not args.no_cpu_baseline and mode == "step" and scheme != L.SCHEME_DILOCO and not adamw:
         def peer_grad(r):
             return synth.scaled_grad_torch(segs, scales, g_std, r, 0)
 

@@ -13,11 +13,14 @@ from .binding import (  # noqa: F401
     VAL_F16,
     VAL_F32,
     VAL_TERNARY,
+    AdamW,
     Config,
     DemoError,
     demo_abi_version,
     demo_decode_apply,
+    demo_decode_apply_adamw,
     demo_encode,
+    demo_encode_adamw,
     demo_payload_layout,
     demo_random_select,
     demo_strerror,

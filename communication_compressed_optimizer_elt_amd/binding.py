@@ -21,7 +21,7 @@ VAL_TERNARY, VAL_F16, VAL_F32 = 0, 1, 2
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, EABI = 0, -1, -2, -3, -4, -5
 
 SYMBOLS = ("demo_abi_version", "demo_strerror", "demo_payload_layout", "demo_encode",
-           "demo_decode_apply", "demo_random_select")
+           "demo_decode_apply", "demo_random_select", "demo_encode_adamw", "demo_decode_apply_adamw")
 
 
 class DemoError(RuntimeError):
@@ -54,6 +54,24 @@ class demo_layout(ctypes.Structure):
 
     def as_dict(self) -> dict:
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class demo_adamw(ctypes.Structure):
+    _fields_ = [("beta2", ctypes.c_float), ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float),
+                ("reserved", ctypes.c_uint32)]
+
+
+@dataclass
+class AdamW:
+    """Python view of demo_adamw (Decoupled AdamW; beta1 is Config.beta)."""
+
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    reserved: int = 0
+
+    def c(self) -> demo_adamw:
+        return demo_adamw(self.beta2, self.eps, self.weight_decay, self.reserved)
 
 
 @dataclass
@@ -104,6 +122,12 @@ def lib() -> ctypes.CDLL:
         L.demo_random_select.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, ctypes.c_uint64,
                                          ctypes.c_uint64, P, P]
         L.demo_random_select.restype = ctypes.c_int
+        L.demo_encode_adamw.argtypes = [ctypes.POINTER(demo_cfg), ctypes.POINTER(demo_adamw), ctypes.c_uint64,
+                                        P, P, P, P, P, P]
+        L.demo_encode_adamw.restype = ctypes.c_int
+        L.demo_decode_apply_adamw.argtypes = [ctypes.POINTER(demo_cfg), ctypes.POINTER(demo_adamw),
+                                              ctypes.c_uint64, P, P, P, ctypes.c_uint64, ctypes.c_uint32, P]
+        L.demo_decode_apply_adamw.restype = ctypes.c_int
         if L.demo_abi_version() != ABI_VERSION:
             raise RuntimeError("libdemo.so ABI version mismatch")
         _lib = L
@@ -177,6 +201,23 @@ def demo_random_select(cfg, seed: int, step: int, n_chunks: int, masks_out, stre
            "demo_random_select")
 
 
+def demo_encode_adamw(cfg, adamw, n_elems: int, grad, moment1, moment2, payload_out, q_out=None,
+                      stream=None) -> None:
+    c = _cfg(cfg)
+    w = adamw.c() if isinstance(adamw, AdamW) else adamw
+    _check(lib().demo_encode_adamw(ctypes.byref(c), ctypes.byref(w), n_elems, _ptr(grad), _ptr(moment1),
+                                   _ptr(moment2), _ptr(payload_out), _ptr(q_out), _stream(stream)),
+           "demo_encode_adamw")
+
+
+def demo_decode_apply_adamw(cfg, adamw, n_elems: int, params, moment2, payloads, stride: int, R: int,
+                            stream=None) -> None:
+    c = _cfg(cfg)
+    w = adamw.c() if isinstance(adamw, AdamW) else adamw
+    _check(lib().demo_decode_apply_adamw(ctypes.byref(c), ctypes.byref(w), n_elems, _ptr(params), _ptr(moment2),
+                                         _ptr(payloads), stride, R, _stream(stream)), "demo_decode_apply_adamw")
+
+
 # raw return codes (tests of the boundary's validation)
 def raw_encode(cfg, n_elems, grad, momentum, payload_out, q_out=None, stream=0) -> int:
     c = _cfg(cfg)
@@ -198,3 +239,19 @@ def raw_payload_layout(cfg, n_elems) -> tuple[int, dict]:
     c = _cfg(cfg)
     rc = int(lib().demo_payload_layout(ctypes.byref(c), n_elems, ctypes.byref(out)))
     return rc, out.as_dict()
+
+
+def raw_encode_adamw(cfg, adamw, n_elems, grad, moment1, moment2, payload_out, q_out=None, stream=0) -> int:
+    c = _cfg(cfg)
+    w = adamw.c() if isinstance(adamw, AdamW) else adamw
+    wp = None if adamw is None else ctypes.byref(w)
+    return int(lib().demo_encode_adamw(ctypes.byref(c), wp, n_elems, grad, moment1, moment2, payload_out, q_out,
+                                       stream))
+
+
+def raw_decode_apply_adamw(cfg, adamw, n_elems, params, moment2, payloads, stride, R, stream=0) -> int:
+    c = _cfg(cfg)
+    w = adamw.c() if isinstance(adamw, AdamW) else adamw
+    wp = None if adamw is None else ctypes.byref(w)
+    return int(lib().demo_decode_apply_adamw(ctypes.byref(c), wp, n_elems, params, moment2, payloads, stride, R,
+                                             stream))

@@ -119,37 +119,74 @@ uint32_t shared_mask(const demo_cfg* cfg) {
 
 int launch_status() { return hipGetLastError() == hipSuccess ? DEMO_OK : DEMO_EHIP; }
 
-template <int KS, int VF>
+// AD: Decoupled AdamW (second moment in EncArgs::v / DecArgs::v)
+template <int KS, int VF, bool AD>
 void launch_encode_dct_q(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
-                           s, a);
+        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true, AD>), dim3(grid), dim3(demo::kBlock),
+                           kEncodeLdsReserve, s, a);
     else
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
-                           s, a);
+        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false, AD>), dim3(grid), dim3(demo::kBlock),
+                           kEncodeLdsReserve, s, a);
 }
 
-template <int VF>
+template <int VF, bool AD>
 void launch_encode_dct(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     switch (a.k) {
-    case 1: launch_encode_dct_q<1, VF>(a, wq, grid, s); break;
-    case 2: launch_encode_dct_q<2, VF>(a, wq, grid, s); break;
+    case 1: launch_encode_dct_q<1, VF, AD>(a, wq, grid, s); break;
+    case 2: launch_encode_dct_q<2, VF, AD>(a, wq, grid, s); break;
     case 3:
-    case 4: launch_encode_dct_q<4, VF>(a, wq, grid, s); break;
+    case 4: launch_encode_dct_q<4, VF, AD>(a, wq, grid, s); break;
     default:
-        if (a.k <= 8) launch_encode_dct_q<8, VF>(a, wq, grid, s);
-        else launch_encode_dct_q<0, VF>(a, wq, grid, s);
+        if (a.k <= 8) launch_encode_dct_q<8, VF, AD>(a, wq, grid, s);
+        else launch_encode_dct_q<0, VF, AD>(a, wq, grid, s);
     }
 }
 
-template <int VF>
+template <int VF, bool AD>
 void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve, s,
-                           a);
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true, AD>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+                           s, a);
     else
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve, s,
-                           a);
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false, AD>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+                           s, a);
+}
+
+// the encode launch for one configuration: momentum only (DiLoCo between
+// syncs), DCT or position selection, by value format
+template <bool AD>
+void launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool wq, hipStream_t s) {
+    if (!sends) {
+        const uint64_t blocks = (a.n / 4 + 3 + 255) / 256;
+        if (wq)
+            hipLaunchKernelGGL((demo::momentum_kernel<true, AD>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((demo::momentum_kernel<false, AD>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+        return;
+    }
+    const unsigned grid = grid_for_groups(a.G);
+    if (cfg->scheme == DEMO_SCHEME_DCT) {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY: launch_encode_dct<demo::VF_TERNARY, AD>(a, wq, grid, s); break;
+        case DEMO_VAL_F16: launch_encode_dct<demo::VF_F16, AD>(a, wq, grid, s); break;
+        default: launch_encode_dct<demo::VF_F32, AD>(a, wq, grid, s); break;
+        }
+    } else {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY: launch_encode_sel<demo::VF_TERNARY, AD>(a, wq, grid, s); break;
+        case DEMO_VAL_F16: launch_encode_sel<demo::VF_F16, AD>(a, wq, grid, s); break;
+        default: launch_encode_sel<demo::VF_F32, AD>(a, wq, grid, s); break;
+        }
+    }
+}
+
+int check_adamw(const demo_adamw* w) {
+    if (!w) return DEMO_EINVAL;
+    if (w->reserved != 0) return DEMO_EINVAL;
+    if (!(w->beta2 >= 0.f && w->beta2 < 1.f)) return DEMO_EINVAL;
+    if (!(w->eps >= 0.f) || !std::isfinite(w->eps) || !std::isfinite(w->weight_decay)) return DEMO_EINVAL;
+    return DEMO_OK;
 }
 
 // Selection-scheme decode with ternary planes: up to this many payload entries
@@ -184,23 +221,31 @@ int demo_payload_layout(const demo_cfg* cfg, uint64_t n_elems, demo_layout* out)
     return DEMO_OK;
 }
 
-int demo_encode(const demo_cfg* cfg, uint64_t n_elems, const float* grad, float* momentum, void* payload_out,
-                float* q_out, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// demo_encode, and with w (second moment v) demo_encode_adamw
+int encode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, const float* grad, float* momentum,
+                float* v, void* payload_out, float* q_out, void* hip_stream) {
     int rc = check_cfg(cfg);
     if (rc) return rc;
     if ((rc = check_size(cfg, n_elems))) return rc;
+    if (w && (rc = check_adamw(w))) return rc;
     const bool sends = cfg->scheme != DEMO_SCHEME_DILOCO || is_sync_step(cfg);
-    if (!grad || !momentum || (sends && !payload_out)) return DEMO_EINVAL;
-    if (!aligned16(grad) || !aligned16(momentum) || (q_out && !aligned16(q_out)) ||
+    if (!grad || !momentum || (w && !v) || (sends && !payload_out)) return DEMO_EINVAL;
+    if (!aligned16(grad) || !aligned16(momentum) || (q_out && !aligned16(q_out)) || (w && !aligned16(v)) ||
         (sends && !aligned16(payload_out)))
         return DEMO_EALIGN;
     demo_layout L;
     layout_of(cfg, n_elems, &L);
     const uint64_t nb = n_elems * 4;
     const uint64_t pb = sends ? L.total_bytes : 0;
+    const uint64_t vb = w ? nb : 0;
     if (overlap(grad, nb, momentum, nb) || overlap(grad, nb, q_out, nb) || overlap(momentum, nb, q_out, nb) ||
         overlap(payload_out, pb, grad, nb) || overlap(payload_out, pb, momentum, nb) ||
-        overlap(payload_out, pb, q_out, nb))
+        overlap(payload_out, pb, q_out, nb) || overlap(v, vb, grad, nb) || overlap(v, vb, momentum, nb) ||
+        overlap(v, vb, q_out, nb) || overlap(v, vb, payload_out, pb))
         return DEMO_EINVAL;
 
     const uint64_t C = (n_elems + 31) / 32;
@@ -221,52 +266,71 @@ int demo_encode(const demo_cfg* cfg, uint64_t n_elems, const float* grad, float*
     a.step_lo = (uint32_t)cfg->step;
     a.mask = shared_mask(cfg);
     a.beta = cfg->beta;
+    a.gamma = w ? 1.f - cfg->beta : 1.f;  // AdamW's first moment weighs g by 1 - beta1
+    a.v = w ? v : nullptr;
+    a.beta2 = w ? w->beta2 : 0.f;
     a.k = slots_per_chunk(cfg);
     a.random = cfg->scheme == DEMO_SCHEME_RANDOM;
     a.sign = (int)cfg->sign;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    const unsigned grid = grid_for_groups(a.G);
     const bool wq = q_out != nullptr;
-
-    if (!sends) {
-        const uint64_t blocks = (n_elems / 4 + 3 + 255) / 256;
-        if (wq)
-            hipLaunchKernelGGL((demo::momentum_kernel<true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((demo::momentum_kernel<false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-        return launch_status();
-    }
-    if (cfg->scheme == DEMO_SCHEME_DCT) {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: launch_encode_dct<demo::VF_TERNARY>(a, wq, grid, s); break;
-        case DEMO_VAL_F16: launch_encode_dct<demo::VF_F16>(a, wq, grid, s); break;
-        default: launch_encode_dct<demo::VF_F32>(a, wq, grid, s); break;
-        }
-    } else {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: launch_encode_sel<demo::VF_TERNARY>(a, wq, grid, s); break;
-        case DEMO_VAL_F16: launch_encode_sel<demo::VF_F16>(a, wq, grid, s); break;
-        default: launch_encode_sel<demo::VF_F32>(a, wq, grid, s); break;
-        }
-    }
+    if (w)
+        launch_encode<true>(cfg, a, sends, wq, s);
+    else
+        launch_encode<false>(cfg, a, sends, wq, s);
     return launch_status();
 }
 
-int demo_decode_apply(const demo_cfg* cfg, uint64_t n_elems, float* params, const void* payloads, uint64_t stride,
-                      uint32_t R, void* hip_stream) {
+template <bool AD>
+void launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+    const uint64_t entries = (uint64_t)a.R * (uint64_t)a.k;  // payload entries per chunk
+    if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY, AD>), grid, block, 0, s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16, AD>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32, AD>), grid, block, 0, s, a); break;
+        }
+    } else if (cfg->scheme == DEMO_SCHEME_DCT) {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>), grid, block, 0, s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16, AD>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32, AD>), grid, block, 0, s, a); break;
+        }
+    } else {
+        switch (cfg->value_fmt) {
+        case DEMO_VAL_TERNARY:
+            if (entries > kSelScalarEntries)
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>), grid, block, 0, s, a);
+            else
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>), grid, block, 0, s, a);
+            break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false, AD>), grid, block, 0, s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false, AD>), grid, block, 0, s, a); break;
+        }
+    }
+}
+
+// demo_decode_apply, and with w (second moment v) demo_decode_apply_adamw
+int decode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, float* params, const float* v,
+                const void* payloads, uint64_t stride, uint32_t R, void* hip_stream) {
     int rc = check_cfg(cfg);
     if (rc) return rc;
     if ((rc = check_size(cfg, n_elems))) return rc;
+    if (w && (rc = check_adamw(w))) return rc;
     if (R < 1 || R > (1u << 20)) return DEMO_EINVAL;
     const bool sends = cfg->scheme != DEMO_SCHEME_DILOCO || is_sync_step(cfg);
-    if (!params || (sends && !payloads)) return DEMO_EINVAL;
-    if (!aligned16(params) || (sends && (!aligned16(payloads) || (stride & 15u) != 0))) return DEMO_EALIGN;
+    if (!params || (w && !v) || (sends && !payloads)) return DEMO_EINVAL;
+    if (!aligned16(params) || (w && !aligned16(v)) ||
+        (sends && (!aligned16(payloads) || (stride & 15u) != 0)))
+        return DEMO_EALIGN;
     demo_layout L;
     layout_of(cfg, n_elems, &L);
     if (!sends) return DEMO_OK;
     if (stride < L.total_bytes) return DEMO_EINVAL;
     if ((uint64_t)(R - 1) > (UINT64_MAX - L.total_bytes) / (stride ? stride : 1)) return DEMO_EINVAL;
-    if (overlap(params, n_elems * 4, payloads, (uint64_t)(R - 1) * stride + L.total_bytes)) return DEMO_EINVAL;
+    const uint64_t payb = (uint64_t)(R - 1) * stride + L.total_bytes;
+    if (overlap(params, n_elems * 4, payloads, payb) || (w && overlap(params, n_elems * 4, v, n_elems * 4)))
+        return DEMO_EINVAL;
 
     const uint64_t C = (n_elems + 31) / 32;
     DecArgs a{};
@@ -286,37 +350,51 @@ int demo_decode_apply(const demo_cfg* cfg, uint64_t n_elems, float* params, cons
     a.mask = shared_mask(cfg);
     a.lr = cfg->lr;
     a.invR = 1.0f / (float)R;
+    if (w) {  // AdamW bias corrections of step t = step + 1, in double, then fp32
+        const double t = (double)cfg->step + 1.0;
+        a.v = v;
+        a.c1 = (float)(1.0 / (1.0 - std::pow((double)cfg->beta, t)));
+        a.c2 = (float)(1.0 / (1.0 - std::pow((double)w->beta2, t)));
+        a.eps = w->eps;
+        a.wd = w->weight_decay;
+    }
     a.k = slots_per_chunk(cfg);
     a.R = (int)R;
     a.random = cfg->scheme == DEMO_SCHEME_RANDOM;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(grid_for_groups(a.G)), block(demo::kBlock);
-    const uint64_t entries = (uint64_t)R * (uint64_t)a.k;  // payload entries per chunk
-    if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY>), grid, block, 0, s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32>), grid, block, 0, s, a); break;
-        }
-    } else if (cfg->scheme == DEMO_SCHEME_DCT) {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY>), grid, block, 0, s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32>), grid, block, 0, s, a); break;
-        }
-    } else {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY:
-            if (entries > kSelScalarEntries)
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true>), grid, block, 0, s, a);
-            else
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false>), grid, block, 0, s, a);
-            break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false>), grid, block, 0, s, a); break;
-        }
-    }
+    if (w)
+        launch_decode<true>(cfg, a, grid, block, s);
+    else
+        launch_decode<false>(cfg, a, grid, block, s);
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int demo_encode(const demo_cfg* cfg, uint64_t n_elems, const float* grad, float* momentum, void* payload_out,
+                float* q_out, void* hip_stream) {
+    return encode_impl(cfg, nullptr, n_elems, grad, momentum, nullptr, payload_out, q_out, hip_stream);
+}
+
+int demo_encode_adamw(const demo_cfg* cfg, const demo_adamw* adamw, uint64_t n_elems, const float* grad,
+                      float* moment1, float* moment2, void* payload_out, float* q_out, void* hip_stream) {
+    if (!adamw) return DEMO_EINVAL;
+    return encode_impl(cfg, adamw, n_elems, grad, moment1, moment2, payload_out, q_out, hip_stream);
+}
+
+int demo_decode_apply(const demo_cfg* cfg, uint64_t n_elems, float* params, const void* payloads, uint64_t stride,
+                      uint32_t R, void* hip_stream) {
+    return decode_impl(cfg, nullptr, n_elems, params, nullptr, payloads, stride, R, hip_stream);
+}
+
+int demo_decode_apply_adamw(const demo_cfg* cfg, const demo_adamw* adamw, uint64_t n_elems, float* params,
+                            const float* moment2, const void* payloads, uint64_t stride, uint32_t R,
+                            void* hip_stream) {
+    if (!adamw) return DEMO_EINVAL;
+    return decode_impl(cfg, adamw, n_elems, params, moment2, payloads, stride, R, hip_stream);
 }
 
 int demo_random_select(const demo_cfg* cfg, uint64_t seed, uint64_t step, uint64_t n_chunks, uint32_t* masks_out,

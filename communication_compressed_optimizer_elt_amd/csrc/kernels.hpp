@@ -27,6 +27,9 @@ struct EncArgs {
     uint32_t step_lo;
     uint32_t mask;  // shared positions of STRIDE / DILOCO
     float beta;
+    float gamma;    // u = beta*m + gamma*g: 1, or 1 - beta1 for AdamW's first moment
+    float* v;       // AdamW second moment (nullptr: plain momentum)
+    float beta2;
     int k;
     int random;     // 1: positions from random_mask per chunk
     int sign;       // 1: slots carry sign(value); 0: the value itself
@@ -44,6 +47,8 @@ struct DecArgs {
     float lr, invR;
     int k, R;
     int random;
+    const float* v;         // AdamW second moment (nullptr: theta -= lr*Q)
+    float c1, c2, eps, wd;  // AdamW bias corrections 1/(1-beta^t), eps, weight decay
 };
 
 // ---------------------------------------------------------------- streaming --
@@ -56,7 +61,14 @@ __device__ __forceinline__ float4 load_stream(const float4* p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
-// u = beta*m + g for the wave's group, coalesced order; zero beyond n.
+// AdamW second moment: beta2*v + (1 - beta2)*g^2
+__device__ __forceinline__ float second_moment(const EncArgs& a, float v, float g) {
+    return fmaf(a.beta2, v, (1.f - a.beta2) * (g * g));
+}
+
+// u = beta*m + gamma*g for the wave's group, coalesced order; zero beyond n
+// (with AdamW the second moment is updated in the same pass).
+template <bool AD>
 __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool full, int lane, float4 (&uc)[8]) {
     if (full) {
         const float4* g4 = reinterpret_cast<const float4*>(a.g + base);
@@ -67,12 +79,24 @@ __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool ful
             gv[r] = load_stream(g4 + r * kWave + lane);
             mv[r] = m4[r * kWave + lane];
         }
+        if constexpr (AD) {
+            float4* v4 = reinterpret_cast<float4*>(a.v + base);
+#pragma unroll
+            for (int r = 0; r < 8; r++) {
+                float4 vv = v4[r * kWave + lane];
+                vv.x = second_moment(a, vv.x, gv[r].x);
+                vv.y = second_moment(a, vv.y, gv[r].y);
+                vv.z = second_moment(a, vv.z, gv[r].z);
+                vv.w = second_moment(a, vv.w, gv[r].w);
+                v4[r * kWave + lane] = vv;
+            }
+        }
 #pragma unroll
         for (int r = 0; r < 8; r++) {
-            uc[r].x = fmaf(a.beta, mv[r].x, gv[r].x);
-            uc[r].y = fmaf(a.beta, mv[r].y, gv[r].y);
-            uc[r].z = fmaf(a.beta, mv[r].z, gv[r].z);
-            uc[r].w = fmaf(a.beta, mv[r].w, gv[r].w);
+            uc[r].x = fmaf(a.beta, mv[r].x, AD ? a.gamma * gv[r].x : gv[r].x);
+            uc[r].y = fmaf(a.beta, mv[r].y, AD ? a.gamma * gv[r].y : gv[r].y);
+            uc[r].z = fmaf(a.beta, mv[r].z, AD ? a.gamma * gv[r].z : gv[r].z);
+            uc[r].w = fmaf(a.beta, mv[r].w, AD ? a.gamma * gv[r].w : gv[r].w);
         }
     } else {
 #pragma unroll
@@ -81,7 +105,11 @@ __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool ful
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 const uint64_t e = base + r * 256 + lane * 4 + t;
-                v[t] = (e < a.n) ? fmaf(a.beta, a.m[e], a.g[e]) : 0.f;
+                v[t] = 0.f;
+                if (e < a.n) {
+                    if constexpr (AD) a.v[e] = second_moment(a, a.v[e], a.g[e]);
+                    v[t] = fmaf(a.beta, a.m[e], AD ? a.gamma * a.g[e] : a.g[e]);
+                }
             }
             uc[r] = make_float4(v[0], v[1], v[2], v[3]);
         }
@@ -168,7 +196,7 @@ __device__ __forceinline__ uint16_t wire_f16(float v, int sign) {
 //         transform from the LDS basis table.
 // KS = 0: any k, selection mask, q by the full inverse transform.
 
-template <int KS, int VF, bool WQ>
+template <int KS, int VF, bool WQ, bool AD>
 __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
     __shared__ float tab[kChunk * kTabStride];
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
@@ -188,7 +216,7 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
         const bool valid = c < a.C;
 
         float4 uc[8];
-        load_u(a, base, full, lane, uc);
+        load_u<AD>(a, base, full, lane, uc);
         wave_lds_sync();
         put_coalesced(st, lane, uc);
         wave_lds_sync();
@@ -430,7 +458,7 @@ __device__ __forceinline__ void store_slot_raw(uint8_t* val, uint64_t c, int k, 
 
 // ---------------------------------------- encode (Random / Striding / DiLoCo) --
 
-template <int VF, bool WQ>
+template <int VF, bool WQ, bool AD>
 __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     const int lane = threadIdx.x & (kWave - 1);
@@ -447,7 +475,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
         const bool valid = c < a.C;
 
         float4 uc[8];
-        load_u(a, base, full, lane, uc);
+        load_u<AD>(a, base, full, lane, uc);
         wave_lds_sync();
         put_coalesced(st, lane, uc);
         wave_lds_sync();
@@ -516,7 +544,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
 // DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.  One
 // float4 per thread; the threads past the last float4 take the 0-3 trailing
 // elements.
-template <bool WQ>
+template <bool WQ, bool AD>
 __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
     const uint64_t n4 = a.n / 4;
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -524,15 +552,25 @@ __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
         const float4 gv = load_stream(reinterpret_cast<const float4*>(a.g) + i);
         float4* m4 = reinterpret_cast<float4*>(a.m);
         float4 mv = m4[i];
-        mv.x = fmaf(a.beta, mv.x, gv.x);
-        mv.y = fmaf(a.beta, mv.y, gv.y);
-        mv.z = fmaf(a.beta, mv.z, gv.z);
-        mv.w = fmaf(a.beta, mv.w, gv.w);
+        if constexpr (AD) {
+            float4* v4 = reinterpret_cast<float4*>(a.v);
+            float4 vv = v4[i];
+            vv.x = second_moment(a, vv.x, gv.x);
+            vv.y = second_moment(a, vv.y, gv.y);
+            vv.z = second_moment(a, vv.z, gv.z);
+            vv.w = second_moment(a, vv.w, gv.w);
+            v4[i] = vv;
+        }
+        mv.x = fmaf(a.beta, mv.x, AD ? a.gamma * gv.x : gv.x);
+        mv.y = fmaf(a.beta, mv.y, AD ? a.gamma * gv.y : gv.y);
+        mv.z = fmaf(a.beta, mv.z, AD ? a.gamma * gv.z : gv.z);
+        mv.w = fmaf(a.beta, mv.w, AD ? a.gamma * gv.w : gv.w);
         m4[i] = mv;
         if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     } else if (i - n4 < (a.n & 3)) {
         const uint64_t e = n4 * 4 + (i - n4);
-        a.m[e] = fmaf(a.beta, a.m[e], a.g[e]);
+        if constexpr (AD) a.v[e] = second_moment(a, a.v[e], a.g[e]);
+        a.m[e] = fmaf(a.beta, a.m[e], AD ? a.gamma * a.g[e] : a.g[e]);
         if (WQ) a.q_out[e] = 0.f;
     }
 }
@@ -625,21 +663,44 @@ __device__ __forceinline__ float slot_value(const DecArgs& a, const uint8_t* pr,
     }
 }
 
-// theta <- theta - lr * Q with Q in coalesced order from the LDS tile
+// One parameter's update: theta - lr*Q, or with AdamW
+// theta - lr*(c1*Q/(sqrt(c2*v) + eps) + wd*theta).
+template <bool AD>
+__device__ __forceinline__ float param_step(const DecArgs& a, float th, float q, float v) {
+    if constexpr (AD) return th - a.lr * (a.c1 * q / (sqrtf(a.c2 * v) + a.eps) + a.wd * th);
+    return fmaf(-a.lr, q, th);
+}
+
+__device__ __forceinline__ float4 adamw_step4(const DecArgs& a, float4 th, float4 q, float4 v) {
+    return make_float4(param_step<true>(a, th.x, q.x, v.x), param_step<true>(a, th.y, q.y, v.y),
+                       param_step<true>(a, th.z, q.z, v.z), param_step<true>(a, th.w, q.w, v.w));
+}
+
+// theta <- theta - lr * Q (param_step) with Q in coalesced order from the LDS tile
+template <bool AD>
 __device__ __forceinline__ void apply_update(const DecArgs& a, const float* st, uint64_t base, bool full, int lane) {
     float4 qc[8];
     get_coalesced(st, lane, qc);
     if (full) {
         float4* t4 = reinterpret_cast<float4*>(a.theta + base);
-        float4 tv[8];
+        float4 tv[8], vv[8];
 #pragma unroll
         for (int r = 0; r < 8; r++) tv[r] = t4[r * kWave + lane];
+        if constexpr (AD) {
+            const float4* v4 = reinterpret_cast<const float4*>(a.v + base);
+#pragma unroll
+            for (int r = 0; r < 8; r++) vv[r] = v4[r * kWave + lane];
+        }
 #pragma unroll
         for (int r = 0; r < 8; r++) {
-            tv[r].x = fmaf(-a.lr, qc[r].x, tv[r].x);
-            tv[r].y = fmaf(-a.lr, qc[r].y, tv[r].y);
-            tv[r].z = fmaf(-a.lr, qc[r].z, tv[r].z);
-            tv[r].w = fmaf(-a.lr, qc[r].w, tv[r].w);
+            if constexpr (AD)
+                tv[r] = adamw_step4(a, tv[r], qc[r], vv[r]);
+            else {
+                tv[r].x = fmaf(-a.lr, qc[r].x, tv[r].x);
+                tv[r].y = fmaf(-a.lr, qc[r].y, tv[r].y);
+                tv[r].z = fmaf(-a.lr, qc[r].z, tv[r].z);
+                tv[r].w = fmaf(-a.lr, qc[r].w, tv[r].w);
+            }
             t4[r * kWave + lane] = tv[r];
         }
     } else {
@@ -649,7 +710,7 @@ __device__ __forceinline__ void apply_update(const DecArgs& a, const float* st, 
 #pragma unroll
             for (int t = 0; t < 4; t++) {
                 const uint64_t e = base + r * 256 + lane * 4 + t;
-                if (e < a.n) a.theta[e] = fmaf(-a.lr, qq[t], a.theta[e]);
+                if (e < a.n) a.theta[e] = param_step<AD>(a, a.theta[e], qq[t], AD ? a.v[e] : 0.f);
             }
         }
     }
@@ -671,15 +732,22 @@ __device__ __forceinline__ void prefetch_theta(const DecArgs& a, uint64_t base, 
     }
 }
 
+template <bool AD>
 __device__ __forceinline__ void apply_update_prefetched(const DecArgs& a, const float* st, uint64_t base, bool full,
                                                         int lane, ThetaTile& t) {
     if (!full) {
-        apply_update(a, st, base, full, lane);
+        apply_update<AD>(a, st, base, full, lane);
         return;
     }
     float4 qc[8];
     get_coalesced(st, lane, qc);
     float4* t4 = reinterpret_cast<float4*>(a.theta + base);
+    if constexpr (AD) {
+        const float4* v4 = reinterpret_cast<const float4*>(a.v + base);
+#pragma unroll
+        for (int r = 0; r < 8; r++) t4[r * kWave + lane] = adamw_step4(a, t.v[r], qc[r], v4[r * kWave + lane]);
+        return;
+    }
 #pragma unroll
     for (int r = 0; r < 8; r++) {
         float4 tv = t.v[r];
@@ -749,7 +817,7 @@ __device__ __forceinline__ int staged_ternary(const uint4* ws, int e, int lane) 
 // directly from basis rows of an LDS table.
 constexpr int kSparseEntries = 8;
 
-template <int VF>
+template <int VF, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     __shared__ float tab[kChunk * kTabStride];
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
@@ -785,7 +853,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     for (int i = 0; i < 32; i++) Q[i] *= a.invR;
     put_chunk(st, lane, Q);
     wave_lds_sync();
-    apply_update(a, st, base, full, lane);
+    apply_update<AD>(a, st, base, full, lane);
 }
 
 // DCT scheme, many entries per chunk: the entries are summed per frequency in
@@ -829,7 +897,7 @@ __device__ __forceinline__ void stage_index(const DecArgs& a, uint64_t grp, uint
         if (ok[i]) *reinterpret_cast<uint4*>(is + (lane + i * kWave) * 16) = v[i];
 }
 
-template <int VF>
+template <int VF, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     __shared__ uint4 words_all[VF == VF_TERNARY ? kWavesPerBlock * kWave : 1];
@@ -936,7 +1004,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     wave_lds_sync();
     put_chunk(st, lane, Q);
     wave_lds_sync();
-    apply_update_prefetched(a, st, base, full, lane, th);
+    apply_update_prefetched<AD>(a, st, base, full, lane, th);
 }
 
 // ---- bit-sliced counting of ternary planes over many replicas -------------
@@ -1070,7 +1138,7 @@ __device__ __forceinline__ void count_ternary(const DecArgs& a, uint64_t grp, fl
 // written once to its position in the lane's LDS tile and the tile updates
 // theta in coalesced order.
 
-template <int VF, bool STAGED>
+template <int VF, bool STAGED, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
     const int lane = threadIdx.x & (kWave - 1);
@@ -1149,7 +1217,7 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
             st[swz(lane, (int)j)] = valid ? A[s] * a.invR : 0.f;
         }
     wave_lds_sync();
-    apply_update_prefetched(a, st, base, full, lane, th);
+    apply_update_prefetched<AD>(a, st, base, full, lane, th);
 }
 
 // ------------------------------------------------------------------ select --

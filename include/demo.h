@@ -107,6 +107,25 @@ typedef struct demo_layout {
     uint64_t total_bytes; /* minimum stride between replicas */
 } demo_layout;
 
+/*
+ * Decoupled AdamW (DeToNATION notes, "Decoupled AdamW": an AdamW variant whose
+ * first and second moments are not synchronised).  The notes give no formula;
+ * the reading implemented: both moments stay local and are never exchanged;
+ * the first moment m = beta1*m + (1-beta1)*g (beta1 = demo_cfg.beta) takes the
+ * momentum's place in the extraction, the payload and the error feedback of
+ * demo_encode; v = beta2*v + (1-beta2)*g^2; the decode applies the exchanged
+ * mean Q as AdamW applies its first moment:
+ *   theta -= lr * ((Q / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
+ *                  + weight_decay * theta),   t = demo_cfg.step + 1.
+ * beta2 in [0, 1); eps >= 0 and weight_decay finite; reserved must be 0.
+ */
+typedef struct demo_adamw {
+    float beta2;
+    float eps;
+    float weight_decay;
+    uint32_t reserved;
+} demo_adamw;
+
 /* Library version; equals DEMO_ABI_VERSION. */
 int demo_abi_version(void);
 
@@ -146,6 +165,26 @@ int demo_encode(const demo_cfg *cfg, uint64_t n_elems, const float *grad, float 
  */
 int demo_decode_apply(const demo_cfg *cfg, uint64_t n_elems, float *params, const void *payloads,
                       uint64_t stride, uint32_t R, void *hip_stream);
+
+/*
+ * demo_encode for Decoupled AdamW (see demo_adamw): moment1 [n_elems] is the
+ * first moment (extracted from and updated in place like demo_encode's
+ * momentum), moment2 [n_elems] the second moment, updated in place (also on
+ * DiLoCo steps without a payload).  16-byte aligned; no argument may alias
+ * another.  Same payload, codes and asynchrony as demo_encode.
+ */
+int demo_encode_adamw(const demo_cfg *cfg, const demo_adamw *adamw, uint64_t n_elems, const float *grad,
+                      float *moment1, float *moment2, void *payload_out, float *q_out, void *hip_stream);
+
+/*
+ * demo_decode_apply for Decoupled AdamW: the same Q, applied with this
+ * replica's second moment moment2 [n_elems] (read-only, 16-byte aligned, not
+ * aliasing params) and weight decay, as stated at demo_adamw.  On a DILOCO
+ * non-sync step nothing is read or written.
+ */
+int demo_decode_apply_adamw(const demo_cfg *cfg, const demo_adamw *adamw, uint64_t n_elems, float *params,
+                            const float *moment2, const void *payloads, uint64_t stride, uint32_t R,
+                            void *hip_stream);
 
 /*
  * Shared-seed slot positions of n_chunks chunks (global ids chunk_offset +

@@ -26,6 +26,9 @@ correct, which tolerance applies) are the ones stated for the optimizer step:
   lr/R times the sum over replicas and slots of |value difference| times the
   largest basis entry (0.25 for the DCT, 1 for positions); that allowance
   accumulates over the steps.
+* Decoupled AdamW (adamw given): the second moment v is compared like m,
+  relative to the chunk's max v; the operand scale of u = beta1*m +
+  (1-beta1)*g is max(beta1 |m| + (1-beta1) |g|).
 """
 from __future__ import annotations
 
@@ -46,6 +49,10 @@ def oracle_params(cfg: L.Config) -> oracle.Params:
                          value_fmt=cfg.value_fmt, beta=cfg.beta, lr=cfg.lr, seed=cfg.seed, step=cfg.step)
 
 
+def oracle_adamw(w: L.AdamW | None) -> oracle.AdamW | None:
+    return None if w is None else oracle.AdamW(beta2=w.beta2, eps=w.eps, weight_decay=w.weight_decay)
+
+
 @dataclass
 class Report:
     steps: int = 0
@@ -55,17 +62,18 @@ class Report:
     max_err_m: float = 0.0
     max_err_q: float = 0.0
     max_err_theta: float = 0.0
+    max_err_v: float = 0.0
     value_roundings: int = 0
     payload_bytes_compared: int = 0
     failures: list = field(default_factory=list)
 
     def ok(self) -> bool:
-        return not self.failures and max(self.max_err_m, self.max_err_q, self.max_err_theta) <= TOL
+        return not self.failures and max(self.max_err_m, self.max_err_q, self.max_err_theta, self.max_err_v) <= TOL
 
     def summary(self) -> str:
         return (f"steps={self.steps} chunks={self.chunks_checked} near_ties={self.near_ties} "
                 f"sign_exc={self.sign_exceptions} value_roundings={self.value_roundings} err_m={self.max_err_m:.3g} err_q={self.max_err_q:.3g} "
-                f"err_theta={self.max_err_theta:.3g} payload_bytes={self.payload_bytes_compared} "
+                f"err_theta={self.max_err_theta:.3g} err_v={self.max_err_v:.3g} payload_bytes={self.payload_bytes_compared} "
                 f"failures={len(self.failures)}" + ("" if not self.failures else f" first: {self.failures[0]}"))
 
 
@@ -88,7 +96,8 @@ class ParityRun:
     """R replicas of one shard on one GPU (replica 0 is this GPU's own), with a
     shared theta, mirrored by R oracle shards over a chunk sample."""
 
-    def __init__(self, cfg: L.Config, n: int, R: int, sample=None, with_q: bool = False, device="cuda"):
+    def __init__(self, cfg: L.Config, n: int, R: int, sample=None, with_q: bool = False, device="cuda",
+                 adamw: L.AdamW | None = None):
         import torch
 
         self.torch = torch
@@ -104,6 +113,8 @@ class ParityRun:
         self.stride = self.layout["total_bytes"]
         self.pay = torch.zeros(R * self.stride, dtype=torch.uint8, device=device)
         self.m = [None] * R
+        self.v = [None] * R
+        self.adamw = adamw
         self.theta = None
         self.q = [torch.zeros(n, dtype=torch.float32, device=device) for _ in range(R)] if with_q else None
         self.nvalid = np.full(len(self.sample), CHUNK, np.int32)
@@ -114,38 +125,55 @@ class ParityRun:
         self.report = Report()
         self.shards = None
 
-    def set_state(self, m0_list, theta0):
-        """m0_list: R flat fp32 device tensors; theta0: flat fp32 device tensor."""
+    def set_state(self, m0_list, theta0, v0_list=None):
+        """m0_list (and v0_list, AdamW's second moments; zeros if None): R flat
+        fp32 device tensors; theta0: flat fp32 device tensor."""
+        import torch
+
         self.m = [m.clone() for m in m0_list]
         self.theta = theta0.clone()
+        if self.adamw is not None:
+            self.v = ([v.clone() for v in v0_list] if v0_list is not None else
+                      [torch.zeros_like(m) for m in self.m])
         ids = self.sample.astype(np.uint64) + np.uint64(self.cfg.chunk_offset)
         th_rows = _chunk_rows(self.theta, self.n, self.sample)
-        self.shards = [oracle.Shard(ids, self.nvalid, _chunk_rows(m, self.n, self.sample), th_rows)
-                       for m in self.m]
+        self.shards = [oracle.Shard(ids, self.nvalid, _chunk_rows(m, self.n, self.sample), th_rows,
+                                    None if self.adamw is None else _chunk_rows(self.v[r], self.n, self.sample))
+                       for r, m in enumerate(self.m)]
 
     # ------------------------------------------------------------------ #
     def step(self, t: int, grads, check: bool = True, decode: bool = True):
         torch = self.torch
         cfg = self.cfg
         cfg.step = t
+        w = self.adamw
         for r in range(self.R):
-            L.demo_encode(cfg, self.n, grads[r], self.m[r], self.pay[r * self.stride:],
-                          self.q[r] if self.with_q else None)
+            q = self.q[r] if self.with_q else None
+            if w is None:
+                L.demo_encode(cfg, self.n, grads[r], self.m[r], self.pay[r * self.stride:], q)
+            else:
+                L.demo_encode_adamw(cfg, w, self.n, grads[r], self.m[r], self.v[r], self.pay[r * self.stride:], q)
         if decode:
-            L.demo_decode_apply(cfg, self.n, self.theta, self.pay, self.stride, self.R)
+            if w is None:
+                L.demo_decode_apply(cfg, self.n, self.theta, self.pay, self.stride, self.R)
+            else:
+                L.demo_decode_apply_adamw(cfg, w, self.n, self.theta, self.v[0], self.pay, self.stride, self.R)
         torch.cuda.synchronize()
 
         p = oracle_params(cfg)
+        ow = oracle_adamw(w)
         outs = []
         self.op_scale = []
         beta = np.float64(np.float32(cfg.beta))
+        gamma = 1.0 if w is None else 1.0 - beta
         for r in range(self.R):
             g_rows = _chunk_rows(grads[r], self.n, self.sample)
-            self.op_scale.append(np.max(beta * np.abs(self.shards[r].m) + np.abs(g_rows.astype(np.float64)), axis=1))
-            outs.append(self.shards[r].encode(p, g_rows))
+            self.op_scale.append(np.max(beta * np.abs(self.shards[r].m) + gamma * np.abs(g_rows.astype(np.float64)),
+                                        axis=1))
+            outs.append(self.shards[r].encode(p, g_rows, ow))
         if decode:
             # theta is shared by the replicas; the oracle keeps it in shard 0
-            self.shards[0].decode(p, [o[0] for o in outs], [o[1] for o in outs])
+            self.shards[0].decode(p, [o[0] for o in outs], [o[1] for o in outs], ow)
         self.report.steps += 1
         if check:
             self._compare(p, outs, decode)
@@ -176,7 +204,7 @@ class ParityRun:
                     self.report.value_roundings += int(np.sum(rounded))
                     bmax = 0.25 if p.scheme == oracle.DCT else 1.0
                     self.theta_allow += (np.float64(np.float32(p.lr)) / self.R * bmax *
-                                         np.sum(np.abs(gv - val_o), axis=1))
+                                         np.sum(np.abs(gv - val_o), axis=1) * self._adam_gain(p))
                 if p.scheme == oracle.DCT:
                     same &= np.all(gi == idx_o, axis=1)
                 # chunks already left out after a near-tie follow their own trajectory
@@ -198,6 +226,11 @@ class ParityRun:
             if self.with_q:
                 q_gpu = _chunk_rows(self.q[r], self.n, self.sample).astype(np.float64)
                 rep.max_err_q = max(rep.max_err_q, _scaled_err(q_gpu, q_o, scale, keep, self.nvalid, rep, f"q[{r}]"))
+            if self.adamw is not None:
+                v_gpu = _chunk_rows(self.v[r], self.n, self.sample).astype(np.float64)
+                v_or = self.shards[r].v
+                rep.max_err_v = max(rep.max_err_v, _scaled_err(v_gpu, v_or, np.max(np.abs(v_or), axis=1), keep,
+                                                               self.nvalid, rep, f"v[{r}]"))
         if decode:
             keep = ~self.excluded
             th_gpu = _chunk_rows(self.theta, self.n, self.sample).astype(np.float64)
@@ -207,6 +240,16 @@ class ParityRun:
                                     _scaled_err(th_gpu, th_or, scale, keep, self.nvalid, rep, "theta",
                                                 allow=self.theta_allow))
         rep.chunks_checked += int(np.sum(~self.excluded))
+
+    def _adam_gain(self, p):
+        """Per chunk, the largest factor AdamW puts on Q: c1 / (sqrt(c2 v) + eps)."""
+        if self.adamw is None:
+            return 1.0
+        t = p.step + 1
+        b1, b2 = np.float64(np.float32(p.beta)), np.float64(np.float32(self.adamw.beta2))
+        c1, c2 = 1.0 / (1.0 - b1 ** t), 1.0 / (1.0 - b2 ** t)
+        eps = np.float64(np.float32(self.adamw.eps))
+        return np.max(c1 / (np.sqrt(c2 * self.shards[0].v) + eps), axis=1)
 
     def _diagnose(self, p, r, i, gi, gv, io, vo, X, u_scale):
         """A chunk whose slots differ: a near-tie or a near-zero sign, or a failure."""

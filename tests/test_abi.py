@@ -152,3 +152,25 @@ def test_plain_c_client(lib, tmp_path):
     ref = oracle.payload_regions(oracle.Params(scheme=oracle.DCT, k=1), 639697920)
     for key in ("idx_off", "idx_bytes", "nz_off", "neg_off", "plane_bytes", "val_off", "val_bytes"):
         assert got[key] == ref[key], key
+
+
+def test_adamw_validation(lib):
+    cfg = _cfg(k=2)
+    W = L.AdamW()
+    g, m, v, pay = A, 2 * A, 3 * A, 4 * A
+    assert L.raw_encode_adamw(cfg, None, 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, L.AdamW(beta2=1.0), 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, L.AdamW(beta2=-0.5), 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, L.AdamW(eps=-1.0), 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, L.AdamW(weight_decay=float("nan")), 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, L.AdamW(reserved=1), 1024, g, m, v, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, W, 1024, g, m, None, pay) == L.EINVAL
+    assert L.raw_encode_adamw(cfg, W, 1024, g, m, v + 4, pay) == L.EALIGN
+    assert L.raw_encode_adamw(cfg, W, 1024, g, m, g + 1024, pay) == L.EINVAL  # v overlaps grad
+    assert L.raw_encode_adamw(cfg, W, 1024, g, m, pay + 16, pay) == L.EINVAL  # v overlaps the payload
+    lay = L.demo_payload_layout(cfg, 1024)
+    assert L.raw_decode_apply_adamw(cfg, None, 1024, A, v, pay, lay["total_bytes"], 2) == L.EINVAL
+    assert L.raw_decode_apply_adamw(cfg, W, 1024, A, None, pay, lay["total_bytes"], 2) == L.EINVAL
+    assert L.raw_decode_apply_adamw(cfg, W, 1024, A, v + 8, pay, lay["total_bytes"], 2) == L.EALIGN
+    assert L.raw_decode_apply_adamw(cfg, W, 1024, A, A + 2048, pay, lay["total_bytes"], 2) == L.EINVAL
+    assert L.raw_decode_apply_adamw(_cfg(abi_version=2), W, 1024, A, v, pay, lay["total_bytes"], 2) == L.EABI

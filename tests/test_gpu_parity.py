@@ -46,8 +46,8 @@ def _host_state(torch, n, R, seed_base=0, m_std=1.0, g_std=1.0, theta_std=0.02):
     return m0, th, grads
 
 
-def _run(torch, cfg, n, R, steps, start=0, sample=None, with_q=True, **state_kw):
-    run = ParityRun(cfg, n, R, sample=sample, with_q=with_q)
+def _run(torch, cfg, n, R, steps, start=0, sample=None, with_q=True, adamw=None, **state_kw):
+    run = ParityRun(cfg, n, R, sample=sample, with_q=with_q, adamw=adamw)
     m0, th, grads = _host_state(torch, n, R, **state_kw)
     run.set_state(m0, th)
     for t in range(start, start + steps):
@@ -157,6 +157,31 @@ def test_sign_off_fp16_subnormal_values(torch_cuda, scheme, k):
     assert np.sum((np.abs(val) < 2.0 ** -14) & (val != 0)) > val.size // 2
 
 
+@pytest.mark.parametrize("scheme,k,fmt,sign,R", [
+    (L.SCHEME_DCT, 4, L.VAL_TERNARY, 1, 2),
+    (L.SCHEME_DCT, 1, L.VAL_TERNARY, 1, 9),     # many-entry decode
+    (L.SCHEME_DCT, 2, L.VAL_F32, 0, 2),         # values themselves
+    (L.SCHEME_RANDOM, 8, L.VAL_TERNARY, 1, 2),
+    (L.SCHEME_RANDOM, 16, L.VAL_F32, 1, 2),
+    (L.SCHEME_RANDOM, 8, L.VAL_TERNARY, 1, 17),  # bit-sliced counts
+    (L.SCHEME_STRIDE, 8, L.VAL_F16, 1, 2),
+    (L.SCHEME_DILOCO, 32, L.VAL_TERNARY, 1, 2),
+])
+def test_decoupled_adamw(torch_cuda, scheme, k, fmt, sign, R):
+    """Decoupled AdamW: local first and second moments, the first moment
+    extracted and fed back, Q applied with AdamW's scaling and decay."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=sign, period=4, seed=9)
+    w = L.AdamW(beta2=0.999, eps=1e-8, weight_decay=0.01)
+    _run(torch_cuda, cfg, 32 * 64 * 3 + 17, R, 6, adamw=w)
+
+
+def test_decoupled_adamw_eps_and_tail(torch_cuda):
+    """eps comparable to sqrt(v) and a ragged last chunk."""
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=3)
+    w = L.AdamW(beta2=0.99, eps=1e-3, weight_decay=0.1)
+    _run(torch_cuda, cfg, 4099, 2, 4, adamw=w, g_std=1e-3, m_std=1e-3)
+
+
 def test_zero_and_constant_chunks(torch_cuda):
     """All-zero chunks (every coefficient ties: positions 0..k-1, sign 0) and
     constant chunks (only the DC term survives)."""
@@ -244,10 +269,10 @@ def _device_state(torch, segs, R, g_std, theta_std=0.02, scales=None):
     return n, m0, th, grads
 
 
-def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None, full_first=0):
+def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None, full_first=0, adamw=None):
     n, m0, th, grads = _device_state(torch, segs, R, g_std, scales=scales)
     C = n // 32
-    run = ParityRun(cfg, n, R, sample=_sample(C, sample_every, edge), with_q=False)
+    run = ParityRun(cfg, n, R, sample=_sample(C, sample_every, edge), with_q=False, adamw=adamw)
     run.set_state(m0, th)
     for t in range(steps):
         run.step(t, grads(t))
@@ -280,6 +305,13 @@ def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
     cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt)
     segs = synth.olmo2_half_shard()
     _run_full(torch_cuda, cfg, segs, 2, 3, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
+
+
+def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda):
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    segs = synth.olmo2_half_shard()
+    _run_full(torch_cuda, cfg, segs, 2, 4, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18),
+              adamw=L.AdamW())
 
 
 def test_olmo2_whole_model_on_one_shard(torch_cuda):
