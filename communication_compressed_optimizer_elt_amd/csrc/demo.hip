@@ -6,8 +6,9 @@
 #include <cmath>
 #include <cstdint>
 
+#include "decode.hpp"
 #include "demo.h"
-#include "kernels.hpp"
+#include "encode.hpp"
 
 namespace {
 
