@@ -174,3 +174,18 @@ def test_adamw_validation(lib):
     assert L.raw_decode_apply_adamw(cfg, W, 1024, A, v + 8, pay, lay["total_bytes"], 2) == L.EALIGN
     assert L.raw_decode_apply_adamw(cfg, W, 1024, A, A + 2048, pay, lay["total_bytes"], 2) == L.EINVAL
     assert L.raw_decode_apply_adamw(_cfg(abi_version=2), W, 1024, A, v, pay, lay["total_bytes"], 2) == L.EABI
+
+
+def test_profiled_traffic_is_within_ten_percent_of_the_algorithmic_bytes():
+    """The committed rocprofv3 traffic summaries (profiles/traffic_*.json,
+    FETCH_SIZE and WRITE_SIZE scaled by the same counters on a plain copy)
+    agree with the byte accounting bench.py reports, within 10%."""
+    import glob
+    import json
+
+    files = glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json"))
+    assert files
+    for f in files:
+        rec = json.load(open(f))
+        ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+        assert 0.9 <= ratio <= 1.1, (os.path.basename(f), ratio)

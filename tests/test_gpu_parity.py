@@ -247,6 +247,55 @@ def test_encode_decode_are_deterministic(torch_cuda):
     assert outs[0] == outs[1]
 
 
+@pytest.mark.parametrize("scheme,k,adam", [
+    (L.SCHEME_DCT, 2, False), (L.SCHEME_RANDOM, 8, False), (L.SCHEME_DILOCO, 32, False), (L.SCHEME_DCT, 1, True),
+])
+def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, tmp_path):
+    """The whole optimizer state is (theta, m, v, step): the selection hash has
+    no state of its own.  Running 2N steps straight and running N steps,
+    saving the state to disk, restoring it into fresh buffers and running N
+    more give bit-identical state and payloads."""
+    torch = torch_cuda
+    n, R, N = 32 * 64 * 7 + 9, 2, 6
+    w = L.AdamW() if adam else None
+
+    def fresh(cfg):
+        run = ParityRun(cfg, n, R, sample=np.arange(4), with_q=False, adamw=w)
+        m0, th, grads = _host_state(torch, n, R)
+        run.set_state(m0, th)
+        return run, grads
+
+    cfg = L.Config(scheme=scheme, k=k, period=4, seed=5)
+    straight, grads = fresh(cfg)
+    for t in range(2 * N):
+        straight.step(t, grads(t), check=False)
+
+    first, grads = fresh(L.Config(scheme=scheme, k=k, period=4, seed=5))
+    for t in range(N):
+        first.step(t, grads(t), check=False)
+    saved = {"theta": first.theta.cpu(), "step": N}
+    for r in range(R):
+        saved[f"m{r}"] = first.m[r].cpu()
+        if adam:
+            saved[f"v{r}"] = first.v[r].cpu()
+    torch.save(saved, tmp_path / "state.pt")
+    del first
+
+    loaded = torch.load(tmp_path / "state.pt", weights_only=True)
+    resumed, grads = fresh(L.Config(scheme=scheme, k=k, period=4, seed=5))
+    resumed.set_state([loaded[f"m{r}"].cuda() for r in range(R)], loaded["theta"].cuda(),
+                      [loaded[f"v{r}"].cuda() for r in range(R)] if adam else None)
+    for t in range(loaded["step"], 2 * N):
+        resumed.step(t, grads(t), check=False)
+
+    assert torch.equal(resumed.theta, straight.theta)
+    for r in range(R):
+        assert torch.equal(resumed.m[r], straight.m[r])
+        if adam:
+            assert torch.equal(resumed.v[r], straight.v[r])
+    assert torch.equal(resumed.pay, straight.pay)
+
+
 # --------------------------------------------------------- full-size shards --
 
 def _sample(C, every, edge):
