@@ -77,11 +77,33 @@ class Report:
                 f"failures={len(self.failures)}" + ("" if not self.failures else f" first: {self.failures[0]}"))
 
 
+# torch's gather kernel (index_select) faults on tensors of 2^32 or more
+# elements on this stack; above this size rows are copied run by run instead
+_GATHER_LIMIT = 2**31
+
+
+def _chunk_rows_by_runs(t, n, sample):
+    """_chunk_rows through contiguous runs of sampled chunks: each run is one
+    slice copied to the host, with no device-side index kernel."""
+    sample = np.asarray(sample, np.int64)
+    out = np.zeros((len(sample), CHUNK), np.float32)
+    if len(sample) == 0:
+        return out
+    breaks = np.nonzero(np.diff(sample) != 1)[0] + 1
+    for a, b in zip(np.r_[0, breaks], np.r_[breaks, len(sample)]):
+        e0 = int(sample[a]) * CHUNK
+        e1 = min((int(sample[b - 1]) + 1) * CHUNK, n)
+        out[a:b].reshape(-1)[: e1 - e0] = t[e0:e1].cpu().numpy()
+    return out
+
+
 def _chunk_rows(t, n, sample):
     """Rows [len(sample)][32] (fp32, host) of a flat device tensor, tail zero-padded."""
     import torch
 
     C = (n + CHUNK - 1) // CHUNK
+    if C * CHUNK >= _GATHER_LIMIT:
+        return _chunk_rows_by_runs(t, n, sample)
     if n % CHUNK:
         pad = torch.zeros(C * CHUNK, dtype=t.dtype, device=t.device)
         pad[:n] = t[:n]

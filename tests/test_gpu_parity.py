@@ -363,6 +363,37 @@ def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda):
               adamw=L.AdamW())
 
 
+def test_shard_beyond_2_pow_32_elements(torch_cuda):
+    """n = 2^32 + 40 elements (17 GB per fp32 array, a ragged last chunk of 8):
+    every element, chunk and group index passes 32 bits; sampled chunks around
+    the 2^31 and 2^32 element marks and at both ends, DeMo k=1, R=2."""
+    torch = torch_cuda
+    if torch.cuda.get_device_properties(0).total_memory < 200 * 2**30:
+        pytest.skip("needs about 160 GB of device memory")
+    n = 2**32 + 40
+    C = (n + 31) // 32
+    marks = [2**31 // 32, 2**32 // 32]
+    sample = np.unique(np.r_[0:2048, C - 2048:C, [m + d for m in marks for d in range(-1024, 1024)],
+                             0:C:999983])
+    sample = sample[sample < C]
+    R = 2
+    m0 = [torch.zeros(n, dtype=torch.float32, device="cuda") for _ in range(R)]
+    th = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
+    g = [torch.empty(n, dtype=torch.float32, device="cuda") for _ in range(R)]
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    run = ParityRun(cfg, n, R, sample=sample, with_q=False)
+    run.set_state(m0, th)
+    del m0, th
+    for t in range(2):
+        for r in range(R):
+            synth.normal_torch(n, 1e-3, r, synth.TAG_GRAD, t, out=g[r])
+        run.step(t, g)
+    print(run.report.summary(), flush=True)
+    assert run.report.ok(), run.report.summary()
+    del run, g
+    torch.cuda.empty_cache()
+
+
 def test_olmo2_whole_model_on_one_shard(torch_cuda):
     """The shard is the whole OLMo2-1B-shaped model (1,279,395,840 parameters,
     one replica per shard group), DeMo k = 1, R = 2, sampled chunks."""
