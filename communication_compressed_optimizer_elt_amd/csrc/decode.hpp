@@ -7,6 +7,7 @@
 #include "kernels.hpp"
 
 namespace demo {
+
 // ------------------------------------------------------------------ decode --
 
 // Words of a payload, which no kernel of the launch writes, read through the
@@ -59,7 +60,7 @@ __device__ __forceinline__ void add_slot_values(const uint8_t* val, uint32_t lof
     }
 }
 
-
+// this lane's slot value from a plane word pair: NZ ? (NEG ? -1 : +1) : 0
 __device__ __forceinline__ float ternary_of(uint64_t nzw, uint64_t negw, int lane) {
     const bool nz = (nzw >> lane) & 1ull;
     const bool ng = (negw >> lane) & 1ull;

@@ -6,6 +6,7 @@
 #include "kernels.hpp"
 
 namespace demo {
+
 // ------------------------------------------------------------ encode (DCT) --
 //
 // KS > 0: k <= KS, selection by k argmax passes, q by sparse inverse
