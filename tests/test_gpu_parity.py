@@ -296,6 +296,53 @@ def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, t
     assert torch.equal(resumed.pay, straight.pay)
 
 
+@pytest.mark.parametrize("scheme,k,R", [(L.SCHEME_DCT, 1, 2), (L.SCHEME_DCT, 2, 9), (L.SCHEME_RANDOM, 8, 17)])
+def test_hip_graph_replays_match_eager_calls(torch_cuda, scheme, k, R):
+    """demo_encode + demo_decode_apply captured once into a HIP graph (the
+    library launches kernels only: no allocation, no memset) and replayed
+    several times, with eager work and synchronisation between replays; after
+    every replay the state and payloads equal those of the same calls made
+    eagerly, bit for bit."""
+    torch = torch_cuda
+    n = 32 * 64 * 9 + 5
+    cfg = L.Config(scheme=scheme, k=k, seed=4, step=3)
+    stride = L.demo_payload_layout(cfg, n)["total_bytes"]
+
+    def state():
+        g = torch.from_numpy(synth.normal_np(n, 1.0, 0, synth.TAG_GRAD)).cuda()
+        m = torch.from_numpy(synth.normal_np(n, 1.0, 0, synth.TAG_MOM)).cuda()
+        th = torch.from_numpy(synth.normal_np(n, 0.02, 0, synth.TAG_THETA)).cuda()
+        pay = torch.zeros(R * stride, dtype=torch.uint8, device="cuda")
+        for r in range(1, R):  # the other replicas' payloads, fixed
+            pm = torch.from_numpy(synth.normal_np(n, 1.0, r, synth.TAG_MOM)).cuda()
+            L.demo_encode(cfg, n, torch.from_numpy(synth.normal_np(n, 1.0, r, synth.TAG_GRAD)).cuda(), pm,
+                          pay[r * stride:])
+        torch.cuda.synchronize()
+        return g, m, th, pay
+
+    def one_step(g, m, th, pay, stream):
+        L.demo_encode(cfg, n, g, m, pay, None, stream)
+        L.demo_decode_apply(cfg, n, th, pay, stride, R, stream)
+
+    eg, em, eth, epay = state()
+    gg, gm, gth, gpay = state()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        one_step(gg, gm, gth, gpay, s)
+    torch.cuda.synchronize()
+    for i in range(4):
+        one_step(eg, em, eth, epay, None)
+        graph.replay()
+        junk = torch.randn(1 << 16, device="cuda").sum()  # eager work between replays
+        torch.cuda.synchronize()
+        assert float(junk) == float(junk)
+        assert torch.equal(gm, em), i
+        assert torch.equal(gth, eth), i
+        assert torch.equal(gpay, epay), i
+
+
 # --------------------------------------------------------- full-size shards --
 
 def _sample(C, every, edge):
