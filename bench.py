@@ -266,18 +266,38 @@ def cpu_baseline(cfg, n, g, m, theta, peer_grad, R, budget_s):
         gi, gv, _, _ = peer.encode(p, peer_grad(r)[: S * 32].view(S, 32).cpu().numpy())
         peers_idx.append(gi)
         peers_val.append(gv)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        idx, val, _, _ = own.encode(p, g_rows)
-        own.decode(p, [idx] + peers_idx, [val] + peers_val)
-        steps += 1
-        if time.perf_counter() - t0 >= budget_s or steps >= 50:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": S * 32 * steps / dt, "unit": "params/s", "cores": oracle.threads(), "kind": "oracle",
+    def timed_steps(budget, max_steps):
+        steps = 0
+        t0 = time.perf_counter()
+        while True:
+            idx, val, _, _ = own.encode(p, g_rows)
+            own.decode(p, [idx] + peers_idx, [val] + peers_val)
+            steps += 1
+            if time.perf_counter() - t0 >= budget or steps >= max_steps:
+                return steps, time.perf_counter() - t0
+
+    cores = oracle.threads()
+    steps, dt = timed_steps(budget_s, 50)
+    # the same oracle on one core, over a shorter run
+    oracle.set_threads(1)
+    steps1, dt1 = timed_steps(budget_s / 3, 50)
+    oracle.set_threads(cores)
+    return {"value": S * 32 * steps / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
             "sample": f"first {S} chunks ({S * 32} params) of the shard, {steps} encode+decode steps "
-                      f"in {dt:.1f} s, fp64 state"}
+                      f"in {dt:.1f} s, fp64 state",
+            "single_core_value": S * 32 * steps1 / dt1,
+            "host": {"cpu": _cpu_model(), "nproc": os.cpu_count()}}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":

@@ -98,6 +98,8 @@ def lib():
         P = ctypes.c_void_p
         L.oracle_threads.argtypes = []
         L.oracle_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_threads.restype = None
         L.oracle_basis.argtypes = [P]
         L.oracle_dct.argtypes = [P, P]
         L.oracle_idct.argtypes = [P, P]
@@ -150,6 +152,10 @@ def _ptr(a: np.ndarray | None):
 def threads() -> int:
     """OpenMP threads the oracle's loops use."""
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 def basis() -> np.ndarray:

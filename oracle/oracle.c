@@ -85,6 +85,9 @@ typedef struct oracle_adamw {
 /* threads the OpenMP loops below run on */
 int oracle_threads(void) { return omp_get_max_threads(); }
 
+/* run the loops below on n threads (timing the oracle on one core) */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+
 /* ------------------------------------------------------------------------ */
 /* DCT-II basis, straight from its definition.                               */
 /* ------------------------------------------------------------------------ */
