@@ -343,6 +343,38 @@ def test_hip_graph_replays_match_eager_calls(torch_cuda, scheme, k, R):
         assert torch.equal(gpay, epay), i
 
 
+def _random_configs(count, seed):
+    """Seeded mixes of scheme, slots, format, sign, replicas, AdamW, offset, size."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(count):
+        scheme = int(rng.integers(0, 4))
+        if scheme == L.SCHEME_STRIDE:
+            k = int(rng.choice([1, 2, 4, 8, 16, 32]))
+        else:
+            k = int(rng.integers(1, 33))
+        fmt = int(rng.integers(0, 3))
+        sign = 1 if fmt == L.VAL_TERNARY else int(rng.integers(0, 2))
+        R = int(rng.choice([1, 2, 3, 5, 9, 17, 33]))
+        adam = bool(rng.integers(0, 4) == 0)
+        n = int(rng.integers(1, 32 * 64 * 4))
+        offset = int(rng.integers(0, 2**40))
+        period = int(rng.integers(1, 5))
+        out.append((i, scheme, k, fmt, sign, R, adam, n, offset, period))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_configs(40, 20261202), ids=lambda c: f"case{c[0]}")
+def test_random_configurations(torch_cuda, case):
+    """A seeded sweep over the configuration space: every combination of
+    scheme, slot count, payload format, sign, replica count, optimizer, chunk
+    offset and ragged size that the draw produces must match the oracle."""
+    _, scheme, k, fmt, sign, R, adam, n, offset, period = case
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=sign, period=period, seed=offset % 977,
+                   chunk_offset=offset)
+    _run(torch_cuda, cfg, n, R, 3, adamw=L.AdamW(weight_decay=0.05) if adam else None)
+
+
 # --------------------------------------------------------- full-size shards --
 
 def _sample(C, every, edge):
