@@ -56,14 +56,33 @@ ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1"}
 DILOCO_PERIOD = 16
 
 
+def _elf_section(path: str, wanted: str) -> bytes:
+    """Bytes of one section of a 64-bit little-endian ELF file (our own build)."""
+    import struct
+
+    with open(path, "rb") as f:
+        data = f.read()
+    shoff, = struct.unpack_from("<Q", data, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", data, 0x3A)
+    def header(i):
+        name, _, _, _, off, size = struct.unpack_from("<IIQQQQ", data, shoff + i * shentsize)
+        return name, off, size
+    _, str_off, _ = header(shstrndx)
+    for i in range(shnum):
+        name, off, size = header(i)
+        end = data.index(b"\0", str_off + name)
+        if data[str_off + name:end].decode() == wanted:
+            return data[off:off + size]
+    raise KeyError(wanted)
+
+
 def library_hash() -> str:
-    """SHA-256 prefix of the built libdemo.so: a traffic record taken with rocprofv3
-    applies only to the exact kernels it measured (the build is reproducible, so
-    comment-only source edits keep the hash)."""
+    """SHA-256 prefix of the device code in the built libdemo.so (its .hip_fatbin
+    section): a traffic record taken with rocprofv3 applies only to the exact
+    kernels it measured; host-side and comment-only changes keep the hash."""
     from communication_compressed_optimizer_elt_amd import binding
 
-    with open(binding.LIB_PATH, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    return hashlib.sha256(_elf_section(binding.LIB_PATH, ".hip_fatbin")).hexdigest()[:16]
 
 
 def main() -> int:
@@ -77,8 +96,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU's shard only; run it with --gpus 1 "
-              "(the step has no cross-GPU part in this build)", file=sys.stderr)
+        print("bench.py measures the optimizer step on one GPU's shard only; run it with --gpus 1 "
+              "(libdemo has no cross-GPU part: the exchange between replicas is simulated)", file=sys.stderr)
         return 2
 
     import torch

@@ -206,7 +206,7 @@ const char* demo_strerror(int code) {
     case DEMO_OK: return "ok";
     case DEMO_EINVAL: return "invalid argument or configuration";
     case DEMO_EALIGN: return "pointer or stride misaligned";
-    case DEMO_EUNSUPPORTED: return "configuration not supported by this build";
+    case DEMO_EUNSUPPORTED: return "configuration not supported by this library version";
     case DEMO_EHIP: return "HIP runtime or launch error";
     case DEMO_EABI: return "demo_cfg.abi_version does not match the library";
     default: return "unknown error code";

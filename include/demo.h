@@ -57,7 +57,7 @@ enum {
     DEMO_OK = 0,
     DEMO_EINVAL = -1,       /* bad configuration value, size or null pointer */
     DEMO_EALIGN = -2,       /* pointer or stride not aligned as required      */
-    DEMO_EUNSUPPORTED = -3, /* valid request this build does not implement    */
+    DEMO_EUNSUPPORTED = -3, /* valid request this library does not implement  */
     DEMO_EHIP = -4,         /* HIP launch / runtime error                     */
     DEMO_EABI = -5          /* cfg->abi_version != DEMO_ABI_VERSION           */
 };

@@ -7,7 +7,7 @@
  * the benchmark use it.  It shares no code, header, table or constant with the
  * GPU library; it is written directly from the method description.
  *
- * Sources (the pages this build follows):
+ * Sources (the pages this oracle follows):
  *  - DeToNATION paper notes (Paper-Notes, AAAI 2026), "Method / FlexDeMo
  *    optimizer", Algorithm 1: momentum m <- beta*m + Delta, extract the fast
  *    components q of m by DCT-II (or another scheme), m <- m - q, synchronise q
