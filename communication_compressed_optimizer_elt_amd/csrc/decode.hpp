@@ -620,20 +620,30 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
         }
 #pragma unroll
         for (int s = 0; s < 32; s++) A[s] = (float)T[s];
-    } else {
+    } else if (VF != VF_TERNARY) {
+        // value formats: two replicas' values loaded before either is added
+        // (measured 3-6% faster than one replica at a time)
+        const uint64_t voff = a.val_off + group_entry(a, grp, 0) * (VF == VF_F32 ? 4 : 2);
+        int r = 0;
+        for (; r + 1 < R; r += 2) {
+            float V0[32], V1[32];
+#pragma unroll
+            for (int s = 0; s < 32; s++) V0[s] = V1[s] = 0.f;
+            add_slot_values<VF>(a.pay + (uint64_t)r * a.stride + voff, loff, k, V0);
+            add_slot_values<VF>(a.pay + (uint64_t)(r + 1) * a.stride + voff, loff, k, V1);
+#pragma unroll
+            for (int s = 0; s < 32; s++) A[s] += V0[s] + V1[s];
+        }
+        if (r < R) add_slot_values<VF>(a.pay + (uint64_t)r * a.stride + voff, loff, k, A);
+    } else {  // ternary, few entries: wave-uniform plane words as scalar loads
         for (int r = 0; r < R; r++) {
             const uint8_t* pr = a.pay + (uint64_t)r * a.stride;
-            if (VF == VF_TERNARY) {
 #pragma unroll
-                for (int s = 0; s < 32; s++)
-                    if (s < k) {
-                        const uint64_t wd = grp * (uint64_t)k + s;
-                        A[s] += ternary_of(load_const_u64(pr + a.nz_off, wd), load_const_u64(pr + a.neg_off, wd),
-                                           lane);
-                    }
-            } else {
-                add_slot_values<VF>(pr + a.val_off + group_entry(a, grp, 0) * (VF == VF_F32 ? 4 : 2), loff, k, A);
-            }
+            for (int s = 0; s < 32; s++)
+                if (s < k) {
+                    const uint64_t wd = grp * (uint64_t)k + s;
+                    A[s] += ternary_of(load_const_u64(pr + a.nz_off, wd), load_const_u64(pr + a.neg_off, wd), lane);
+                }
         }
     }
 
