@@ -221,7 +221,7 @@ __device__ __forceinline__ void stage_words(const DecArgs& a, uint64_t grp, uint
         const uint8_t* pr = a.pay + (uint64_t)rc * a.stride;
         const uint64_t word = grp * (uint64_t)a.k + w.ls;
         nzv[i] = reinterpret_cast<const uint64_t*>(pr + a.nz_off)[word];
-        ngv[i] = reinterpret_cast<const uint64_t*>(pr + a.neg_off)[word];
+        ngv[i] = reinterpret_cast<const uint64_t*>(pr + a.neg_off)[word] & nzv[i];  // NZ decides
     }
 #pragma unroll
     for (int i = 0; i < ROUNDS; i++) {
@@ -233,7 +233,7 @@ __device__ __forceinline__ void stage_words(const DecArgs& a, uint64_t grp, uint
 }
 
 // ternary value {-1, 0, 1} of bit sh of the halves h = {nz, neg}: NZ - 2 NEG
-// (NEG implies NZ)
+// (the staged NEG halves are masked with NZ)
 __device__ __forceinline__ int lane_ternary(uint2 h, uint32_t sh) {
     const int nz = (int)__builtin_amdgcn_ubfe(h.x, sh, 1u);
     const int ng = (int)__builtin_amdgcn_ubfe(h.y, sh, 1u);

@@ -94,7 +94,9 @@ typedef struct demo_cfg {
  *                       chunk c at byte c*k+s; the k positions ascend.
  *   NZ   uint64 [G][k]  TERNARY: bit b of word g*k+s is set iff slot s of chunk
  *   NEG  uint64 [G][k]  64g+b is nonzero / negative.  Value = NZ ? (NEG ? -1 :
- *                       +1) : 0.  NEG without NZ and bits of chunks >= C are 0.
+ *                       +1) : 0.  NEG without NZ and bits of chunks >= C are 0
+ *                       (the encoder never sets them; the decoder reads a NEG
+ *                       bit without its NZ bit as 0 and index bytes mod 32).
  *   VAL  fp16|fp32 [C][k] F16/F32: value of slot s of chunk c at entry c*k+s:
  *                       +-1 or 0 with sign 1, the value itself with sign 0.
  * RANDOM, STRIDE and DILOCO carry no IDX: every replica recomputes the slot

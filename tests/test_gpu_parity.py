@@ -375,6 +375,48 @@ def test_random_configurations(torch_cuda, case):
     _run(torch_cuda, cfg, n, R, 3, adamw=L.AdamW(weight_decay=0.05) if adam else None)
 
 
+@pytest.mark.parametrize("scheme,k,R", [
+    (L.SCHEME_DCT, 1, 2),      # few-entry DCT decode
+    (L.SCHEME_DCT, 2, 9),      # many-entry DCT decode (staged words and index bytes)
+    (L.SCHEME_RANDOM, 8, 1),   # scalar plane words
+    (L.SCHEME_RANDOM, 32, 2),  # staged plane words, per-entry sums
+    (L.SCHEME_RANDOM, 8, 17),  # bit-sliced counts
+])
+def test_decode_reads_stray_bits_as_the_format_says(torch_cuda, scheme, k, R):
+    """A NEG bit without its NZ bit reads as 0 and index bytes are taken mod
+    32, on every decode path: a payload with such stray bits added decodes to
+    exactly the theta of the clean payload."""
+    torch = torch_cuda
+    n = 32 * 64 * 5 + 21
+    cfg = L.Config(scheme=scheme, k=k, seed=8)
+    lay = L.demo_payload_layout(cfg, n)
+    stride = lay["total_bytes"]
+    pay = torch.zeros(R * stride, dtype=torch.uint8, device="cuda")
+    for r in range(R):
+        g = torch.from_numpy(synth.normal_np(n, 1.0, r, synth.TAG_GRAD)).cuda()
+        m = torch.from_numpy(synth.normal_np(n, 1.0, r, synth.TAG_MOM)).cuda()
+        L.demo_encode(cfg, n, g, m, pay[r * stride:])
+    host = pay.cpu().numpy().copy()
+    rng = np.random.default_rng(99)
+    for r in range(R):
+        b = host[r * stride:(r + 1) * stride]
+        nz = b[lay["nz_off"]:lay["nz_off"] + lay["plane_bytes"]].view(np.uint64)
+        neg = b[lay["neg_off"]:lay["neg_off"] + lay["plane_bytes"]].view(np.uint64)
+        neg |= rng.integers(0, 2**63, size=neg.size, dtype=np.uint64) & ~nz
+        if scheme == L.SCHEME_DCT:
+            idx = b[lay["idx_off"]:lay["idx_off"] + lay["idx_bytes"]]
+            idx |= (rng.integers(0, 8, size=idx.size) << 5).astype(np.uint8)
+    assert not np.array_equal(host, pay.cpu().numpy())
+    junk = torch.from_numpy(host).cuda()
+    th0 = torch.from_numpy(synth.normal_np(n, 0.02, 0, synth.TAG_THETA)).cuda()
+    clean_th, junk_th = th0.clone(), th0.clone()
+    L.demo_decode_apply(cfg, n, clean_th, pay, stride, R)
+    L.demo_decode_apply(cfg, n, junk_th, junk, stride, R)
+    torch.cuda.synchronize()
+    assert torch.equal(clean_th, junk_th)
+    assert not torch.equal(clean_th, th0)
+
+
 # --------------------------------------------------------- full-size shards --
 
 def _sample(C, every, edge):
