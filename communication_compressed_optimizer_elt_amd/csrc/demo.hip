@@ -15,7 +15,13 @@ namespace {
 using demo::DecArgs;
 using demo::EncArgs;
 
-constexpr uint64_t kMaxElems = (uint64_t)1 << 40;  // 4 TB of fp32 per array
+constexpr uint64_t kMaxElems = DEMO_MAX_ELEMS;
+// the one-pass grids of the group kernels (64 work-items per 2048 elements)
+// must stay below 2^32 work-items at the largest shard
+static_assert((kMaxElems / 2048) * 64 < ((uint64_t)1 << 32), "one-pass grid exceeds 2^32 work-items");
+// the momentum-only kernel: one float4 per work-item and pass, at most this
+// many blocks of 256 (one pass up to 2^33 elements, grid-stride beyond)
+constexpr uint64_t kMomentumMaxBlocks = (uint64_t)1 << 23;
 
 uint64_t up256(uint64_t x) { return (x + 255u) & ~(uint64_t)255u; }
 
@@ -159,7 +165,9 @@ void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) 
 template <bool AD>
 void launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool wq, hipStream_t s) {
     if (!sends) {
-        const uint64_t blocks = (a.n / 4 + 3 + 255) / 256;
+        uint64_t blocks = (a.n / 4 + 255) / 256;
+        if (blocks < 1) blocks = 1;  // n < 4: the trailing elements only
+        if (blocks > kMomentumMaxBlocks) blocks = kMomentumMaxBlocks;
         if (wq)
             hipLaunchKernelGGL((demo::momentum_kernel<true, AD>), dim3((unsigned)blocks), dim3(256), 0, s, a);
         else

@@ -359,13 +359,14 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
 }
 
 // DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.  One
-// float4 per thread; the threads past the last float4 take the 0-3 trailing
-// elements.
+// float4 per work-item and pass over the grid (a single pass unless the grid
+// was capped); work-items 0-2 also take the 0-3 trailing elements.
 template <bool WQ, bool AD>
 __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
     const uint64_t n4 = a.n / 4;
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n4) {
+    const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = i0; i < n4; i += step) {
         const float4 gv = load_stream(reinterpret_cast<const float4*>(a.g) + i);
         float4* m4 = reinterpret_cast<float4*>(a.m);
         float4 mv = m4[i];
@@ -384,8 +385,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
         mv.w = fmaf(a.beta, mv.w, AD ? a.gamma * gv.w : gv.w);
         m4[i] = mv;
         if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    } else if (i - n4 < (a.n & 3)) {
-        const uint64_t e = n4 * 4 + (i - n4);
+    }
+    if (i0 < (a.n & 3)) {
+        const uint64_t e = n4 * 4 + i0;
         if constexpr (AD) a.v[e] = second_moment(a, a.v[e], a.g[e]);
         a.m[e] = fmaf(a.beta, a.m[e], AD ? a.gamma * a.g[e] : a.g[e]);
         if (WQ) a.q_out[e] = 0.f;

@@ -16,8 +16,11 @@
  *
  * Conventions shared by every entry point
  *  - All tensors are flat fp32 arrays of n_elems elements in device memory
- *    (hipMalloc / PyTorch allocations), 16-byte aligned.  The caller owns all
- *    memory; the library never allocates, frees or keeps pointers.
+ *    (hipMalloc / PyTorch allocations), 16-byte aligned, with
+ *    1 <= n_elems <= DEMO_MAX_ELEMS (2^36, 256 GB per array; larger shards
+ *    are split by the caller, for instance at tensor boundaries, each part
+ *    with its own chunk_offset).  The caller owns all memory; the library
+ *    never allocates, frees or keeps pointers.
  *  - A chunk is 32 consecutive elements; C = ceil(n_elems/32) chunks; the last
  *    chunk is zero-padded inside the kernels and padded outputs are dropped.
  *  - Calls are asynchronous on the given HIP stream (hipStream_t passed as
@@ -39,6 +42,7 @@ extern "C" {
 
 #define DEMO_ABI_VERSION 1
 #define DEMO_CHUNK 32
+#define DEMO_MAX_ELEMS ((uint64_t)1 << 36)
 
 /* Replication schemes ("Replication schemes" table of the DeToNATION notes). */
 enum {
@@ -196,7 +200,8 @@ int demo_decode_apply_adamw(const demo_cfg *cfg, const demo_adamw *adamw, uint64
  * chunk_hi, step_lo, (1 << 24) | i/4), draw i taking word i%4 w and picking
  * free position number floor(w*(32-i)/2^32) counted from bit 0.  STRIDE:
  * positions j % (32/k) == step % (32/k).  `seed` and `step` override
- * cfg->seed and cfg->step.  masks_out: device uint32 [n_chunks], 4-byte aligned.
+ * cfg->seed and cfg->step.  masks_out: device uint32 [n_chunks], 4-byte aligned;
+ * 1 <= n_chunks <= DEMO_MAX_ELEMS / 32.
  */
 int demo_random_select(const demo_cfg *cfg, uint64_t seed, uint64_t step, uint64_t n_chunks,
                        uint32_t *masks_out, void *hip_stream);

@@ -104,6 +104,11 @@ def test_bad_sizes_and_pointers(lib):
     assert L.raw_decode_apply(cfg, 1024, A, A + 256, lay["total_bytes"], 2) == L.EINVAL
     # chunk_offset overflow
     assert L.raw_encode(_cfg(chunk_offset=2**64 - 1), 1024, A, 2 * A, 3 * A) == L.EINVAL
+    # the largest shard is 2^36 elements (host-only checks: nothing is launched)
+    assert L.raw_payload_layout(cfg, 2**36)[0] == L.OK
+    assert L.raw_payload_layout(cfg, 2**36 + 1)[0] == L.EINVAL
+    assert L.raw_encode(cfg, 2**36 + 1, A, 2 * A, 3 * A) == L.EINVAL
+    assert L.raw_random_select(_cfg(scheme=L.SCHEME_RANDOM, k=8), 0, 0, 2**31 + 1, A) == L.EINVAL
 
 
 def test_select_validation(lib):

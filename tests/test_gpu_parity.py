@@ -113,6 +113,8 @@ def test_diloco_scheme(torch_cuda, fmt, period):
     (L.SCHEME_DCT, 32, L.VAL_TERNARY, 5),    # 160 entries, two passes of 4 replicas
     (L.SCHEME_DCT, 3, L.VAL_F16, 17),
     (L.SCHEME_DCT, 1, L.VAL_TERNARY, 70),    # more replicas than one staging pass
+    (L.SCHEME_DCT, 1, L.VAL_TERNARY, 255),   # four staging passes, the last one partial
+    (L.SCHEME_DCT, 16, L.VAL_TERNARY, 17),   # 272 entries, 4 replicas per pass
     (L.SCHEME_RANDOM, 32, L.VAL_TERNARY, 17),  # 544 entries: two passes of 16 replicas
     (L.SCHEME_RANDOM, 3, L.VAL_TERNARY, 17),   # 51 entries, 21 replicas per round
     (L.SCHEME_RANDOM, 8, L.VAL_F32, 17),
@@ -127,6 +129,33 @@ def test_many_replicas(torch_cuda, scheme, k, fmt, R):
     the per-replica word staging."""
     cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, period=1, seed=11)
     _run(torch_cuda, cfg, 32 * 64 * 5 + 33, R, 2)
+
+
+@pytest.mark.parametrize("R", [9, 255, 256])
+def test_dct_decode_of_identical_payloads(torch_cuda, R):
+    """R copies of one DeMo k=1 payload put all R entries of a chunk on one
+    frequency, the largest per-frequency sums the many-entry decode forms:
+    the mean is the payload itself, so theta moves as it does after decoding
+    the single payload."""
+    torch = torch_cuda
+    n = 32 * 64 * 3 + 17
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1, seed=3)
+    stride = L.demo_payload_layout(cfg, n)["total_bytes"]
+    one = torch.zeros(stride, dtype=torch.uint8, device="cuda")
+    g = torch.from_numpy(synth.normal_np(n, 1.0, 0, synth.TAG_GRAD)).cuda()
+    m = torch.from_numpy(synth.normal_np(n, 1.0, 0, synth.TAG_MOM)).cuda()
+    L.demo_encode(cfg, n, g, m, one)
+    pay = one.repeat(R)
+    th0 = torch.from_numpy(synth.normal_np(n, 0.02, 0, synth.TAG_THETA)).cuda()
+    th1, thR = th0.clone(), th0.clone()
+    L.demo_decode_apply(cfg, n, th1, one, stride, 1)
+    L.demo_decode_apply(cfg, n, thR, pay, stride, R)
+    torch.cuda.synchronize()
+    step1, stepR = (th0 - th1).double(), (th0 - thR).double()
+    assert step1.abs().max().item() > 0
+    # the same sums; only the fp32 mean (count * (1/R)) and theta's rounding differ
+    ulp_theta = 2.0 ** -23 * th0.abs().max().item()
+    assert (stepR - step1).abs().max().item() <= 1e-6 * step1.abs().max().item() + 2 * ulp_theta
 
 
 @pytest.mark.parametrize("scheme,k,fmt,R", [
@@ -509,6 +538,36 @@ def test_shard_beyond_2_pow_32_elements(torch_cuda):
         for r in range(R):
             synth.normal_torch(n, 1e-3, r, synth.TAG_GRAD, t, out=g[r])
         run.step(t, g)
+    print(run.report.summary(), flush=True)
+    assert run.report.ok(), run.report.summary()
+    del run, g
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("adamw", [None, L.AdamW()])
+def test_momentum_only_steps_beyond_2_pow_33_elements(torch_cuda, adamw):
+    """DiLoCo steps between synchronisations stream one float4 per work-item
+    and pass; at n = 2^33 + 1029 the grid is capped and 257 float4 and one
+    trailing element fall to a second pass.  Sampled chunks at both ends and
+    around the 2^33 element mark, steps 0 and 1 of period 16."""
+    torch = torch_cuda
+    if torch.cuda.get_device_properties(0).total_memory < 200 * 2**30:
+        pytest.skip("needs about 130 GB of device memory")
+    n = 2**33 + 1029
+    C = (n + 31) // 32
+    mark = 2**33 // 32
+    sample = np.unique(np.r_[0:2048, C - 2048:C, mark - 1024:mark + 1024, 0:C:999983])
+    sample = sample[sample < C]
+    cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16)
+    run = ParityRun(cfg, n, 1, sample=sample, with_q=False, adamw=adamw)
+    m0 = synth.normal_torch(n, 1.0, 0, synth.TAG_MOM)
+    th = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
+    run.set_state([m0], th)
+    del m0, th
+    g = torch.empty(n, dtype=torch.float32, device="cuda")
+    for t in range(2):
+        synth.normal_torch(n, 1e-3, 0, synth.TAG_GRAD, t, out=g)
+        run.step(t, [g])
     print(run.report.summary(), flush=True)
     assert run.report.ok(), run.report.summary()
     del run, g
