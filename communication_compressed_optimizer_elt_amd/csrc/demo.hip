@@ -190,9 +190,11 @@ void launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool wq, h
     }
 }
 
-int check_adamw(const demo_adamw* w) {
+// AdamW's bias correction 1/(1 - beta1^t) needs beta1 = cfg->beta in [0, 1)
+int check_adamw(const demo_cfg* cfg, const demo_adamw* w) {
     if (!w) return DEMO_EINVAL;
     if (w->reserved != 0) return DEMO_EINVAL;
+    if (!(cfg->beta >= 0.f && cfg->beta < 1.f)) return DEMO_EINVAL;
     if (!(w->beta2 >= 0.f && w->beta2 < 1.f)) return DEMO_EINVAL;
     if (!(w->eps >= 0.f) || !std::isfinite(w->eps) || !std::isfinite(w->weight_decay)) return DEMO_EINVAL;
     return DEMO_OK;
@@ -240,7 +242,7 @@ int encode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, cons
     int rc = check_cfg(cfg);
     if (rc) return rc;
     if ((rc = check_size(cfg, n_elems))) return rc;
-    if (w && (rc = check_adamw(w))) return rc;
+    if (w && (rc = check_adamw(cfg, w))) return rc;
     const bool sends = cfg->scheme != DEMO_SCHEME_DILOCO || is_sync_step(cfg);
     if (!grad || !momentum || (w && !v) || (sends && !payload_out)) return DEMO_EINVAL;
     if (!aligned16(grad) || !aligned16(momentum) || (q_out && !aligned16(q_out)) || (w && !aligned16(v)) ||
@@ -325,7 +327,7 @@ int decode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, floa
     int rc = check_cfg(cfg);
     if (rc) return rc;
     if ((rc = check_size(cfg, n_elems))) return rc;
-    if (w && (rc = check_adamw(w))) return rc;
+    if (w && (rc = check_adamw(cfg, w))) return rc;
     if (R < 1 || R > (1u << 20)) return DEMO_EINVAL;
     const bool sends = cfg->scheme != DEMO_SCHEME_DILOCO || is_sync_step(cfg);
     if (!params || (w && !v) || (sends && !payloads)) return DEMO_EINVAL;

@@ -123,7 +123,8 @@ typedef struct demo_layout {
  * mean Q as AdamW applies its first moment:
  *   theta -= lr * ((Q / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
  *                  + weight_decay * theta),   t = demo_cfg.step + 1.
- * beta2 in [0, 1); eps >= 0 and weight_decay finite; reserved must be 0.
+ * beta1 (demo_cfg.beta) and beta2 in [0, 1); eps >= 0 and weight_decay finite;
+ * reserved must be 0.
  */
 typedef struct demo_adamw {
     float beta2;

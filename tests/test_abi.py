@@ -169,6 +169,9 @@ def test_adamw_validation(lib):
     assert L.raw_encode_adamw(cfg, L.AdamW(eps=-1.0), 1024, g, m, v, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, L.AdamW(weight_decay=float("nan")), 1024, g, m, v, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, L.AdamW(reserved=1), 1024, g, m, v, pay) == L.EINVAL
+    for beta1 in (1.0, 1.5, -0.1):  # the bias correction 1/(1 - beta1^t) needs beta1 in [0, 1)
+        assert L.raw_encode_adamw(_cfg(k=2, beta=beta1), W, 1024, g, m, v, pay) == L.EINVAL
+        assert L.raw_decode_apply_adamw(_cfg(k=2, beta=beta1), W, 1024, A, v, pay, 4096, 2) == L.EINVAL
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, None, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, v + 4, pay) == L.EALIGN
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, g + 1024, pay) == L.EINVAL  # v overlaps grad
