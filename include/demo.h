@@ -30,6 +30,9 @@
  *    next synchronisation.  No C++ exception crosses the ABI.
  *  - Buffers passed to one call must not overlap.  Calls on distinct buffers
  *    may be made from several threads.
+ *  - Values are not checked: NaN or infinity in an input propagates into that
+ *    chunk's outputs (which slots a DCT chunk with a NaN transform selects is
+ *    unspecified); every memory access stays inside the buffers described.
  */
 #ifndef DEMO_H
 #define DEMO_H
