@@ -109,6 +109,18 @@ unsigned grid_for_groups(uint64_t G) {
 // 2 blocks per CU (160 KB of LDS per CU).
 constexpr size_t kEncodeLdsReserve = 24 * 1024;
 
+// Decoupled AdamW streams one more array (v) through each kernel.  Its DCT
+// encode (24 KB of loads per wave: g, m, v) measured fastest at 1 block per CU
+// (2.21 ms against 2.31 ms at 2 blocks on a 639,697,920-parameter shard), its
+// decode (v beside theta) at 3 blocks (1.41 ms against 1.42 ms at 4).
+constexpr size_t kEncodeAdamwLdsReserve = 48 * 1024;
+constexpr size_t kDecodeAdamwLdsReserve = 16 * 1024;
+
+template <bool AD>
+constexpr size_t encode_lds_reserve() { return AD ? kEncodeAdamwLdsReserve : kEncodeLdsReserve; }
+template <bool AD>
+constexpr size_t decode_lds_reserve() { return AD ? kDecodeAdamwLdsReserve : 0; }
+
 uint32_t stride_mask(uint64_t step, uint32_t n) {
     const uint32_t s = 32 / n;
     const uint32_t off = (uint32_t)(step % s);
@@ -131,10 +143,10 @@ template <int KS, int VF, bool AD>
 void launch_encode_dct_q(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
         hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true, AD>), dim3(grid), dim3(demo::kBlock),
-                           kEncodeLdsReserve, s, a);
+                           encode_lds_reserve<AD>(), s, a);
     else
         hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false, AD>), dim3(grid), dim3(demo::kBlock),
-                           kEncodeLdsReserve, s, a);
+                           encode_lds_reserve<AD>(), s, a);
 }
 
 template <int VF, bool AD>
@@ -153,10 +165,10 @@ void launch_encode_dct(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) 
 template <int VF, bool AD>
 void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     if (wq)
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true, AD>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true, AD>), dim3(grid), dim3(demo::kBlock), encode_lds_reserve<AD>(),
                            s, a);
     else
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false, AD>), dim3(grid), dim3(demo::kBlock), kEncodeLdsReserve,
+        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false, AD>), dim3(grid), dim3(demo::kBlock), encode_lds_reserve<AD>(),
                            s, a);
 }
 
@@ -297,26 +309,26 @@ void launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block,
     const uint64_t entries = (uint64_t)a.R * (uint64_t)a.k;  // payload entries per chunk
     if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY, AD>), grid, block, 0, s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16, AD>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32, AD>), grid, block, 0, s, a); break;
+        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
         }
     } else if (cfg->scheme == DEMO_SCHEME_DCT) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>), grid, block, 0, s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16, AD>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32, AD>), grid, block, 0, s, a); break;
+        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
         }
     } else {
         switch (cfg->value_fmt) {
         case DEMO_VAL_TERNARY:
             if (entries > kSelScalarEntries)
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>), grid, block, 0, s, a);
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>), grid, block, decode_lds_reserve<AD>(), s, a);
             else
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>), grid, block, 0, s, a);
+                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a);
             break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false, AD>), grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false, AD>), grid, block, 0, s, a); break;
+        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
         }
     }
 }
