@@ -325,6 +325,66 @@ def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, t
     assert torch.equal(resumed.pay, straight.pay)
 
 
+def test_calls_from_two_threads_on_their_own_streams(torch_cuda):
+    """Calls on distinct buffers from two host threads, each on a HIP stream of
+    its own, give bit-identical results to the same calls made one after
+    another on the default stream: no state is shared between calls."""
+    import dataclasses
+    import threading
+
+    torch = torch_cuda
+    n = 32 * 64 * 7 + 19
+    steps = 6
+    cfgs = [L.Config(scheme=L.SCHEME_DCT, k=2, seed=1), L.Config(scheme=L.SCHEME_RANDOM, k=8, seed=2),
+            L.Config(scheme=L.SCHEME_DILOCO, period=3), L.Config(scheme=L.SCHEME_DCT, k=12, seed=4)]
+    grads = [[synth.normal_torch(n, 1.0, i, synth.TAG_GRAD, t) for t in range(steps)] for i in range(len(cfgs))]
+    peers = [synth.normal_torch(n, 1.0, 50 + i, synth.TAG_GRAD) for i in range(len(cfgs))]
+
+    def fresh(i):
+        stride = L.demo_payload_layout(cfgs[i], n)["total_bytes"]
+        return {"m": synth.normal_torch(n, 1.0, i, synth.TAG_MOM), "th": synth.normal_torch(n, 0.02, i, synth.TAG_THETA),
+                "pm": torch.zeros(n, device="cuda"), "pay": torch.zeros(2 * stride, dtype=torch.uint8, device="cuda"),
+                "stride": stride}
+
+    def run(i, st, stream):
+        cfg = dataclasses.replace(cfgs[i])
+        for t in range(steps):
+            cfg.step = t
+            L.demo_encode(cfg, n, peers[i], st["pm"], st["pay"][st["stride"]:], None, stream)
+            L.demo_encode(cfg, n, grads[i][t], st["m"], st["pay"], None, stream)
+            L.demo_decode_apply(cfg, n, st["th"], st["pay"], st["stride"], 2, stream)
+
+    serial = [fresh(i) for i in range(len(cfgs))]
+    for i in range(len(cfgs)):
+        run(i, serial[i], None)
+    torch.cuda.synchronize()
+
+    par = [fresh(i) for i in range(len(cfgs))]
+    streams = [torch.cuda.Stream() for _ in cfgs]
+    for s_ in streams:
+        s_.wait_stream(torch.cuda.current_stream())
+    errors = []
+
+    def worker(idx):
+        try:
+            for i in idx:
+                run(i, par[i], streams[i])
+        except Exception as e:  # surfaced by the assertion below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(idx,)) for idx in ((0, 2), (1, 3))]
+    for th_ in threads:
+        th_.start()
+    for th_ in threads:
+        th_.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(len(cfgs)):
+        for key in ("m", "th", "pm", "pay"):
+            assert torch.equal(serial[i][key], par[i][key]), (i, key)
+    assert not torch.equal(serial[0]["th"], synth.normal_torch(n, 0.02, 0, synth.TAG_THETA))
+
+
 @pytest.mark.parametrize("scheme,k,R", [(L.SCHEME_DCT, 1, 2), (L.SCHEME_DCT, 2, 9), (L.SCHEME_RANDOM, 8, 17)])
 def test_hip_graph_replays_match_eager_calls(torch_cuda, scheme, k, R):
     """demo_encode + demo_decode_apply captured once into a HIP graph (the
