@@ -1,8 +1,9 @@
 """ctypes binding of libdemo (include/demo.h): argument marshalling only.
 
 Every computation runs in the HIP kernels of libdemo.so; this module turns
-PyTorch tensors into device pointers and the current HIP stream, and raises
-on error codes.  There is no fallback: if libdemo.so is missing the first call
+PyTorch tensors into device pointers and the current HIP stream, checks that
+each tensor is a contiguous device tensor of the dtype and size the call
+reads or writes (so no kernel can run past it), and raises on error codes.  There is no fallback: if libdemo.so is missing the first call
 raises.
 """
 from __future__ import annotations
@@ -143,13 +144,39 @@ def _check(rc: int, what: str) -> None:
         raise DemoError(rc, what)
 
 
-def _ptr(t) -> int | None:
-    """Device (or host) address of a tensor, None for None."""
-    if t is None:
-        return None
-    if isinstance(t, int):
+def _buf(t, what: str, nbytes: int, fp32: bool = False, elem: int = 0) -> int | None:
+    """Address of t after checking that the kernels stay inside it: a
+    contiguous device tensor of at least nbytes bytes (float32 where fp32,
+    elements of `elem` bytes where given).  None stays None; an int is taken
+    as a raw device address, unchecked."""
+    if t is None or isinstance(t, int):
         return t
+    if not t.is_cuda:
+        raise ValueError(f"{what}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: expected a contiguous tensor")
+    if fp32 and str(t.dtype) != "torch.float32":
+        raise TypeError(f"{what}: expected float32, got {t.dtype}")
+    if elem and t.element_size() != elem:
+        raise TypeError(f"{what}: expected {elem}-byte elements, got {t.dtype}")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what}: holds {have} bytes, the call needs {nbytes}")
     return t.data_ptr()
+
+
+def _payload_bytes(c, n_elems: int) -> int:
+    """One replica's payload size, 0 if the configuration is invalid (the call
+    itself then returns the error code)."""
+    out = demo_layout()
+    if lib().demo_payload_layout(ctypes.byref(c), max(int(n_elems), 0), ctypes.byref(out)) != OK:
+        return 0
+    return int(out.total_bytes)
+
+
+def _sends(c) -> bool:
+    """Whether this step writes and reads payloads (DiLoCo only on sync steps)."""
+    return c.scheme != SCHEME_DILOCO or (c.period >= 1 and c.step % c.period == c.period - 1)
 
 
 def _stream(stream) -> int | None:
@@ -185,37 +212,50 @@ def demo_payload_layout(cfg, n_elems: int) -> dict:
 
 def demo_encode(cfg, n_elems: int, grad, momentum, payload_out, q_out=None, stream=None) -> None:
     c = _cfg(cfg)
-    _check(lib().demo_encode(ctypes.byref(c), n_elems, _ptr(grad), _ptr(momentum), _ptr(payload_out),
-                             _ptr(q_out), _stream(stream)), "demo_encode")
+    nb = 4 * max(int(n_elems), 0)
+    pb = _payload_bytes(c, n_elems) if _sends(c) else 0
+    _check(lib().demo_encode(ctypes.byref(c), n_elems, _buf(grad, "grad", nb, True),
+                             _buf(momentum, "momentum", nb, True), _buf(payload_out, "payload_out", pb),
+                             _buf(q_out, "q_out", nb, True), _stream(stream)), "demo_encode")
 
 
 def demo_decode_apply(cfg, n_elems: int, params, payloads, stride: int, R: int, stream=None) -> None:
     c = _cfg(cfg)
-    _check(lib().demo_decode_apply(ctypes.byref(c), n_elems, _ptr(params), _ptr(payloads), stride, R,
-                                   _stream(stream)), "demo_decode_apply")
+    nb = 4 * max(int(n_elems), 0)
+    pb = (max(int(R), 1) - 1) * int(stride) + _payload_bytes(c, n_elems) if _sends(c) else 0
+    _check(lib().demo_decode_apply(ctypes.byref(c), n_elems, _buf(params, "params", nb, True),
+                                   _buf(payloads, "payloads", pb), stride, R, _stream(stream)), "demo_decode_apply")
 
 
 def demo_random_select(cfg, seed: int, step: int, n_chunks: int, masks_out, stream=None) -> None:
     c = _cfg(cfg)
-    _check(lib().demo_random_select(ctypes.byref(c), seed, step, n_chunks, _ptr(masks_out), _stream(stream)),
-           "demo_random_select")
+    _check(lib().demo_random_select(ctypes.byref(c), seed, step, n_chunks,
+                                    _buf(masks_out, "masks_out", 4 * max(int(n_chunks), 0), elem=4),
+                                    _stream(stream)), "demo_random_select")
 
 
 def demo_encode_adamw(cfg, adamw, n_elems: int, grad, moment1, moment2, payload_out, q_out=None,
                       stream=None) -> None:
     c = _cfg(cfg)
     w = adamw.c() if isinstance(adamw, AdamW) else adamw
-    _check(lib().demo_encode_adamw(ctypes.byref(c), ctypes.byref(w), n_elems, _ptr(grad), _ptr(moment1),
-                                   _ptr(moment2), _ptr(payload_out), _ptr(q_out), _stream(stream)),
-           "demo_encode_adamw")
+    nb = 4 * max(int(n_elems), 0)
+    pb = _payload_bytes(c, n_elems) if _sends(c) else 0
+    _check(lib().demo_encode_adamw(ctypes.byref(c), ctypes.byref(w), n_elems, _buf(grad, "grad", nb, True),
+                                   _buf(moment1, "moment1", nb, True), _buf(moment2, "moment2", nb, True),
+                                   _buf(payload_out, "payload_out", pb), _buf(q_out, "q_out", nb, True),
+                                   _stream(stream)), "demo_encode_adamw")
 
 
 def demo_decode_apply_adamw(cfg, adamw, n_elems: int, params, moment2, payloads, stride: int, R: int,
                             stream=None) -> None:
     c = _cfg(cfg)
     w = adamw.c() if isinstance(adamw, AdamW) else adamw
-    _check(lib().demo_decode_apply_adamw(ctypes.byref(c), ctypes.byref(w), n_elems, _ptr(params), _ptr(moment2),
-                                         _ptr(payloads), stride, R, _stream(stream)), "demo_decode_apply_adamw")
+    nb = 4 * max(int(n_elems), 0)
+    pb = (max(int(R), 1) - 1) * int(stride) + _payload_bytes(c, n_elems) if _sends(c) else 0
+    _check(lib().demo_decode_apply_adamw(ctypes.byref(c), ctypes.byref(w), n_elems,
+                                         _buf(params, "params", nb, True), _buf(moment2, "moment2", nb, True),
+                                         _buf(payloads, "payloads", pb), stride, R, _stream(stream)),
+           "demo_decode_apply_adamw")
 
 
 # raw return codes (tests of the boundary's validation)

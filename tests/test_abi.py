@@ -184,6 +184,22 @@ def test_adamw_validation(lib):
     assert L.raw_decode_apply_adamw(_cfg(abi_version=2), W, 1024, A, v, pay, lay["total_bytes"], 2) == L.EABI
 
 
+def test_binding_refuses_host_tensors(lib):
+    """The Python wrappers pass only device tensors on (checked before any
+    call into the library)."""
+    import torch
+
+    cfg = _cfg(k=2)
+    t = torch.zeros(1024)
+    pay = torch.zeros(L.demo_payload_layout(cfg, 1024)["total_bytes"], dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.demo_encode(cfg, 1024, t, t.clone(), pay)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.demo_decode_apply(cfg, 1024, t, pay, pay.numel(), 1)
+    with pytest.raises(ValueError, match="device tensor"):
+        L.demo_random_select(_cfg(scheme=L.SCHEME_RANDOM, k=8), 0, 0, 8, torch.zeros(8, dtype=torch.int32))
+
+
 def test_profiled_traffic_is_within_ten_percent_of_the_algorithmic_bytes():
     """The committed rocprofv3 traffic summaries (profiles/traffic_*.json,
     FETCH_SIZE and WRITE_SIZE scaled by the same counters on a plain copy)

@@ -325,6 +325,37 @@ def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, t
     assert torch.equal(resumed.pay, straight.pay)
 
 
+def test_binding_checks_dtype_size_and_layout(torch_cuda):
+    """The Python wrappers refuse tensors the kernels would read or write past
+    (wrong dtype, too few bytes, strided views) before anything is launched."""
+    torch = torch_cuda
+    n = 4096
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=2)
+    stride = L.demo_payload_layout(cfg, n)["total_bytes"]
+    f = torch.zeros(n, device="cuda")
+    pay = torch.zeros(2 * stride, dtype=torch.uint8, device="cuda")
+    with pytest.raises(TypeError, match="float32"):
+        L.demo_encode(cfg, n, f.double(), f.clone(), pay)
+    with pytest.raises(TypeError, match="float32"):
+        L.demo_encode(cfg, n, f, f.half(), pay)
+    with pytest.raises(ValueError, match="bytes"):
+        L.demo_encode(cfg, n, f[: n - 1], f.clone(), pay)
+    with pytest.raises(ValueError, match="bytes"):
+        L.demo_encode(cfg, n, f, f.clone(), pay[: stride - 1])
+    with pytest.raises(ValueError, match="contiguous"):
+        L.demo_encode(cfg, n, torch.zeros(2 * n, device="cuda")[::2], f.clone(), pay)
+    with pytest.raises(ValueError, match="bytes"):
+        L.demo_decode_apply(cfg, n, f, pay[: 2 * stride - 1], stride, 2)
+    with pytest.raises(TypeError, match="4-byte"):
+        L.demo_random_select(L.Config(scheme=L.SCHEME_RANDOM, k=8), 0, 0, 16,
+                             torch.zeros(16, dtype=torch.int64, device="cuda"))
+    with pytest.raises(TypeError, match="float32"):
+        L.demo_decode_apply_adamw(cfg, L.AdamW(), n, f, f.double(), pay, stride, 2)
+    # DiLoCo between synchronisations reads and writes no payload
+    L.demo_encode(L.Config(scheme=L.SCHEME_DILOCO, period=4, step=0), n, f, f.clone(), None)
+    torch.cuda.synchronize()
+
+
 def test_calls_from_two_threads_on_their_own_streams(torch_cuda):
     """Calls on distinct buffers from two host threads, each on a HIP stream of
     its own, give bit-identical results to the same calls made one after
