@@ -136,69 +136,73 @@ uint32_t shared_mask(const demo_cfg* cfg) {
     return 0;
 }
 
-int launch_status() { return hipGetLastError() == hipSuccess ? DEMO_OK : DEMO_EHIP; }
+template <class T>
+struct same_type {
+    using type = T;
+};
+
+// One kernel launch through hipLaunchKernel, whose return code belongs to this
+// launch alone (hipGetLastError would also report an error that an earlier,
+// unrelated HIP call left pending on the thread).  The parameter types come
+// from the kernel; the arguments are converted to them.
+template <class... P>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  typename same_type<P>::type... args) {
+    void* argv[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds, s);
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? DEMO_OK : DEMO_EHIP; }
 
 // AD: Decoupled AdamW (second moment in EncArgs::v / DecArgs::v)
 template <int KS, int VF, bool AD>
-void launch_encode_dct_q(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
-    if (wq)
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, true, AD>), dim3(grid), dim3(demo::kBlock),
-                           encode_lds_reserve<AD>(), s, a);
-    else
-        hipLaunchKernelGGL((demo::encode_dct_kernel<KS, VF, false, AD>), dim3(grid), dim3(demo::kBlock),
-                           encode_lds_reserve<AD>(), s, a);
+hipError_t launch_encode_dct_q(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
+    return launch(wq ? demo::encode_dct_kernel<KS, VF, true, AD> : demo::encode_dct_kernel<KS, VF, false, AD>,
+                  dim3(grid), dim3(demo::kBlock), encode_lds_reserve<AD>(), s, a);
 }
 
 template <int VF, bool AD>
-void launch_encode_dct(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
+hipError_t launch_encode_dct(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
     switch (a.k) {
-    case 1: launch_encode_dct_q<1, VF, AD>(a, wq, grid, s); break;
-    case 2: launch_encode_dct_q<2, VF, AD>(a, wq, grid, s); break;
+    case 1: return launch_encode_dct_q<1, VF, AD>(a, wq, grid, s);
+    case 2: return launch_encode_dct_q<2, VF, AD>(a, wq, grid, s);
     case 3:
-    case 4: launch_encode_dct_q<4, VF, AD>(a, wq, grid, s); break;
+    case 4: return launch_encode_dct_q<4, VF, AD>(a, wq, grid, s);
     default:
-        if (a.k <= 8) launch_encode_dct_q<8, VF, AD>(a, wq, grid, s);
-        else launch_encode_dct_q<0, VF, AD>(a, wq, grid, s);
+        if (a.k <= 8) return launch_encode_dct_q<8, VF, AD>(a, wq, grid, s);
+        return launch_encode_dct_q<0, VF, AD>(a, wq, grid, s);
     }
 }
 
 template <int VF, bool AD>
-void launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
-    if (wq)
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, true, AD>), dim3(grid), dim3(demo::kBlock), encode_lds_reserve<AD>(),
-                           s, a);
-    else
-        hipLaunchKernelGGL((demo::encode_sel_kernel<VF, false, AD>), dim3(grid), dim3(demo::kBlock), encode_lds_reserve<AD>(),
-                           s, a);
+hipError_t launch_encode_sel(const EncArgs& a, bool wq, unsigned grid, hipStream_t s) {
+    return launch(wq ? demo::encode_sel_kernel<VF, true, AD> : demo::encode_sel_kernel<VF, false, AD>, dim3(grid),
+                  dim3(demo::kBlock), encode_lds_reserve<AD>(), s, a);
 }
 
 // the encode launch for one configuration: momentum only (DiLoCo between
 // syncs), DCT or position selection, by value format
 template <bool AD>
-void launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool wq, hipStream_t s) {
+hipError_t launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool wq, hipStream_t s) {
     if (!sends) {
         uint64_t blocks = (a.n / 4 + 255) / 256;
         if (blocks < 1) blocks = 1;  // n < 4: the trailing elements only
         if (blocks > kMomentumMaxBlocks) blocks = kMomentumMaxBlocks;
-        if (wq)
-            hipLaunchKernelGGL((demo::momentum_kernel<true, AD>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((demo::momentum_kernel<false, AD>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-        return;
+        return launch(wq ? demo::momentum_kernel<true, AD> : demo::momentum_kernel<false, AD>,
+                      dim3((unsigned)blocks), dim3(256), 0, s, a);
     }
     const unsigned grid = grid_for_groups(a.G);
     if (cfg->scheme == DEMO_SCHEME_DCT) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: launch_encode_dct<demo::VF_TERNARY, AD>(a, wq, grid, s); break;
-        case DEMO_VAL_F16: launch_encode_dct<demo::VF_F16, AD>(a, wq, grid, s); break;
-        default: launch_encode_dct<demo::VF_F32, AD>(a, wq, grid, s); break;
+        case DEMO_VAL_TERNARY: return launch_encode_dct<demo::VF_TERNARY, AD>(a, wq, grid, s);
+        case DEMO_VAL_F16: return launch_encode_dct<demo::VF_F16, AD>(a, wq, grid, s);
+        default: return launch_encode_dct<demo::VF_F32, AD>(a, wq, grid, s);
         }
-    } else {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: launch_encode_sel<demo::VF_TERNARY, AD>(a, wq, grid, s); break;
-        case DEMO_VAL_F16: launch_encode_sel<demo::VF_F16, AD>(a, wq, grid, s); break;
-        default: launch_encode_sel<demo::VF_F32, AD>(a, wq, grid, s); break;
-        }
+    }
+    switch (cfg->value_fmt) {
+    case DEMO_VAL_TERNARY: return launch_encode_sel<demo::VF_TERNARY, AD>(a, wq, grid, s);
+    case DEMO_VAL_F16: return launch_encode_sel<demo::VF_F16, AD>(a, wq, grid, s);
+    default: return launch_encode_sel<demo::VF_F32, AD>(a, wq, grid, s);
     }
 }
 
@@ -297,39 +301,34 @@ int encode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, cons
     a.sign = (int)cfg->sign;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const bool wq = q_out != nullptr;
-    if (w)
-        launch_encode<true>(cfg, a, sends, wq, s);
-    else
-        launch_encode<false>(cfg, a, sends, wq, s);
-    return launch_status();
+    return status_of(w ? launch_encode<true>(cfg, a, sends, wq, s) : launch_encode<false>(cfg, a, sends, wq, s));
 }
 
 template <bool AD>
-void launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+hipError_t launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block, hipStream_t s) {
     const uint64_t entries = (uint64_t)a.R * (uint64_t)a.k;  // payload entries per chunk
+    const size_t lds = decode_lds_reserve<AD>();
     if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_TERNARY, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F16, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_kernel<demo::VF_F32, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        case DEMO_VAL_TERNARY: return launch(demo::decode_dct_kernel<demo::VF_TERNARY, AD>, grid, block, lds, s, a);
+        case DEMO_VAL_F16: return launch(demo::decode_dct_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
+        default: return launch(demo::decode_dct_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
         }
-    } else if (cfg->scheme == DEMO_SCHEME_DCT) {
+    }
+    if (cfg->scheme == DEMO_SCHEME_DCT) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F16, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_dct_dense_kernel<demo::VF_F32, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
+        case DEMO_VAL_TERNARY: return launch(demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>, grid, block, lds, s, a);
+        case DEMO_VAL_F16: return launch(demo::decode_dct_dense_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
+        default: return launch(demo::decode_dct_dense_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
         }
-    } else {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY:
-            if (entries > kSelScalarEntries)
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>), grid, block, decode_lds_reserve<AD>(), s, a);
-            else
-                hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a);
-            break;
-        case DEMO_VAL_F16: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F16, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        default: hipLaunchKernelGGL((demo::decode_sel_kernel<demo::VF_F32, false, AD>), grid, block, decode_lds_reserve<AD>(), s, a); break;
-        }
+    }
+    switch (cfg->value_fmt) {
+    case DEMO_VAL_TERNARY:
+        if (entries > kSelScalarEntries)
+            return launch(demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>, grid, block, lds, s, a);
+        return launch(demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>, grid, block, lds, s, a);
+    case DEMO_VAL_F16: return launch(demo::decode_sel_kernel<demo::VF_F16, false, AD>, grid, block, lds, s, a);
+    default: return launch(demo::decode_sel_kernel<demo::VF_F32, false, AD>, grid, block, lds, s, a);
     }
 }
 
@@ -386,11 +385,7 @@ int decode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, floa
     a.random = cfg->scheme == DEMO_SCHEME_RANDOM;
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(grid_for_groups(a.G)), block(demo::kBlock);
-    if (w)
-        launch_decode<true>(cfg, a, grid, block, s);
-    else
-        launch_decode<false>(cfg, a, grid, block, s);
-    return launch_status();
+    return status_of(w ? launch_decode<true>(cfg, a, grid, block, s) : launch_decode<false>(cfg, a, grid, block, s));
 }
 
 }  // namespace
@@ -432,10 +427,9 @@ int demo_random_select(const demo_cfg* cfg, uint64_t seed, uint64_t step, uint64
     const uint32_t mask = random ? 0u : stride_mask(step, cfg->k);
     uint64_t blocks = (n_chunks + 255) / 256;
     if (blocks > (1u << 20)) blocks = 1u << 20;
-    hipLaunchKernelGGL(demo::select_kernel, dim3((unsigned)blocks), dim3(256), 0,
-                       static_cast<hipStream_t>(hip_stream), masks_out, n_chunks, cfg->chunk_offset, seed,
-                       (uint32_t)step, (int)cfg->k, random, mask);
-    return launch_status();
+    return status_of(launch(demo::select_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                            static_cast<hipStream_t>(hip_stream), masks_out, n_chunks, cfg->chunk_offset, seed,
+                            (uint32_t)step, (int)cfg->k, random, mask));
 }
 
 }  // extern "C"
