@@ -184,6 +184,16 @@ def test_adamw_validation(lib):
     assert L.raw_decode_apply_adamw(_cfg(abi_version=2), W, 1024, A, v, pay, lay["total_bytes"], 2) == L.EABI
 
 
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    """No fallback: without libdemo.so every entry point raises."""
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", os.path.join(ROOT, "no-such-dir", "libdemo.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        L.demo_payload_layout(_cfg(k=2), 1024)
+    with pytest.raises(RuntimeError, match="not built"):
+        L.demo_abi_version()
+
+
 def test_binding_refuses_host_tensors(lib):
     """The Python wrappers pass only device tensors on (checked before any
     call into the library)."""
