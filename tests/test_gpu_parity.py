@@ -559,7 +559,7 @@ def _device_state(torch, segs, R, g_std, theta_std=0.02, scales=None):
     return n, m0, th, grads
 
 
-def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None, full_first=0, adamw=None):
+def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None, adamw=None):
     n, m0, th, grads = _device_state(torch, segs, R, g_std, scales=scales)
     C = n // 32
     run = ParityRun(cfg, n, R, sample=_sample(C, sample_every, edge), with_q=False, adamw=adamw)
@@ -584,6 +584,29 @@ def test_config3_olmo2_half_shard(torch_cuda, k):
     segs = synth.olmo2_half_shard()
     scales = synth.layer_scales(0, 18)
     _run_full(torch_cuda, cfg, segs, 2, 100 if k == 1 else 5, 997, 4096, 1e-3, scales=scales)
+
+
+@pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
+def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k):
+    """Step 0 of the OLMo2-1B half shard, R = 2, against the oracle on all
+    19,990,560 chunks and every payload byte: every group of the one-pass
+    grid (XCD-contiguous block numbering included) is checked, not a sample."""
+    import time
+
+    t0 = time.time()
+    cfg = L.Config(scheme=scheme, k=k)
+    segs = synth.olmo2_half_shard()
+    n, m0, th, grads = _device_state(torch_cuda, segs, 2, 1e-3, scales=synth.layer_scales(0, 18))
+    run = ParityRun(cfg, n, 2, sample=None, with_q=False)
+    assert run.full
+    run.set_state(m0, th)
+    del m0, th
+    run.step(0, grads(0))
+    print(run.report.summary(), f"{time.time() - t0:.1f} s", flush=True)
+    assert run.report.ok(), run.report.summary()
+    assert run.report.payload_bytes_compared > 0 or run.report.near_ties + run.report.sign_exceptions > 0
+    del run
+    torch_cuda.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("scheme,k,fmt", [
