@@ -162,6 +162,8 @@ class ParityRun:
         self.shards = [oracle.Shard(ids, self.nvalid, _chunk_rows(m, self.n, self.sample), th_rows,
                                     None if self.adamw is None else _chunk_rows(self.v[r], self.n, self.sample))
                        for r, m in enumerate(self.m)]
+        # per replica and chunk, the comparison scale of the previous step (none yet)
+        self.prev_scale = [np.zeros(len(self.sample), np.float64) for _ in self.m]
 
     # ------------------------------------------------------------------ #
     def step(self, t: int, grads, check: bool = True, decode: bool = True):
@@ -190,8 +192,13 @@ class ParityRun:
         gamma = 1.0 if w is None else 1.0 - beta
         for r in range(self.R):
             g_rows = _chunk_rows(grads[r], self.n, self.sample)
-            self.op_scale.append(np.max(beta * np.abs(self.shards[r].m) + gamma * np.abs(g_rows.astype(np.float64)),
-                                        axis=1))
+            # The size of the operands of u = beta*m + gamma*g, plus what the GPU's
+            # fp32 m carries over from earlier steps: its difference from the
+            # oracle's m is bounded by the previous step's scale, and u takes
+            # beta times it (so the bound sums every step's, decayed by beta).
+            fresh = np.max(beta * np.abs(self.shards[r].m) + gamma * np.abs(g_rows.astype(np.float64)), axis=1)
+            self.op_scale.append(fresh + beta * self.prev_scale[r])
+            self.prev_scale[r] = self.op_scale[r]
             outs.append(self.shards[r].encode(p, g_rows, ow))
         if decode:
             # theta is shared by the replicas; the oracle keeps it in shard 0
@@ -319,14 +326,17 @@ def _f16_ulp(x):
 
 
 def _values_close(p, gpu, ref, u_scale):
-    """Sign-off slot values: fp32 within TOL of the chunk's max |u|, fp16 within
-    one fp16 unit in the last place of the larger magnitude."""
+    """Sign-off slot values: fp32 within TOL of the chunk's operand scale; fp16
+    within that plus one fp16 unit in the last place of the larger magnitude
+    (the GPU rounds its fp32 value, itself within TOL of the scale, to fp16;
+    the oracle rounds its fp64 value: the two roundings add one unit)."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     d = np.abs(gpu - ref)
+    fp32 = TOL * np.asarray(u_scale, np.float64)
     if p.value_fmt == oracle.F16:
-        return d <= _f16_ulp(np.maximum(np.abs(gpu), np.abs(ref)))
-    return d <= TOL * np.asarray(u_scale, np.float64)
+        return d <= fp32 + _f16_ulp(np.maximum(np.abs(gpu), np.abs(ref)))
+    return d <= fp32
 
 
 def _scaled_err(gpu, ref, scale, keep, nvalid, rep, what, allow=None):
