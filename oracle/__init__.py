@@ -134,6 +134,8 @@ def lib():
         L.oracle_pack.restype = ctypes.c_int
         L.oracle_unpack.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P, P, P]
         L.oracle_unpack.restype = ctypes.c_int
+        L.oracle_unpack_chunks.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P, P, ctypes.c_uint64, P, P]
+        L.oracle_unpack_chunks.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -349,13 +351,23 @@ def pack(p: Params, n_elems: int, idx, val) -> np.ndarray:
     return buf
 
 
-def unpack(p: Params, n_elems: int, buf):
-    """Returns (idx [C][k], val [C][k], ok) where ok is False for a malformed buffer."""
+def unpack(p: Params, n_elems: int, buf, chunks=None):
+    """Returns (idx [C][k], val [C][k], ok) where ok is False for a malformed
+    buffer.  With chunks (chunk ids within the shard) the rows are those
+    chunks' slots, in the order given; ok still covers the whole buffer."""
     buf = np.ascontiguousarray(buf, np.uint8)
     C = (n_elems + CHUNK - 1) // CHUNK
     k = CHUNK if p.scheme == DILOCO else p.k
-    idx = np.zeros((C, k), np.int32)
-    val = np.zeros((C, k), np.float64)
     c = p.c()
-    r = lib().oracle_unpack(ctypes.byref(c), n_elems, _ptr(buf), _ptr(idx), _ptr(val))
+    if chunks is None:
+        idx = np.zeros((C, k), np.int32)
+        val = np.zeros((C, k), np.float64)
+        r = lib().oracle_unpack(ctypes.byref(c), n_elems, _ptr(buf), _ptr(idx), _ptr(val))
+        return idx, val, r == 0
+    ids = np.ascontiguousarray(chunks, np.uint64)
+    idx = np.zeros((len(ids), k), np.int32)
+    val = np.zeros((len(ids), k), np.float64)
+    r = lib().oracle_unpack_chunks(ctypes.byref(c), n_elems, _ptr(buf), _ptr(ids), len(ids), _ptr(idx), _ptr(val))
+    if r == -2:
+        raise IndexError("unpack: chunk id past the shard")
     return idx, val, r == 0

@@ -634,40 +634,47 @@ int oracle_pack(const oracle_params *p, uint64_t n_elems, const int32_t *slot_id
     return 0;
 }
 
-/* inverse of oracle_pack; returns -1 if a NEG bit is set without its NZ bit
- * or a bit beyond the last chunk is set */
-int oracle_unpack(const oracle_params *p, uint64_t n_elems, const uint8_t *buf, int32_t *slot_idx,
-                  double *slot_val)
+/* Inverse of oracle_pack for the chunks listed in chunks[0..nchunks) (all C
+ * chunks in order when chunks is NULL): row i of slot_idx / slot_val receives
+ * chunk chunks[i].  Returns -1 if the buffer is malformed anywhere (a NEG bit
+ * set without its NZ bit, or a plane bit set for a chunk c >= C), whichever
+ * chunks were asked for. */
+int oracle_unpack_chunks(const oracle_params *p, uint64_t n_elems, const uint8_t *buf,
+                         const uint64_t *chunks, uint64_t nchunks, int32_t *slot_idx, double *slot_val)
 {
     uint64_t reg[8];
     oracle_payload_regions(p, n_elems, reg);
     uint64_t C = (n_elems + OR_CHUNK - 1) / OR_CHUNK;
     uint64_t G = (C + 63) / 64;
     int k = (p->scheme == OR_DILOCO) ? OR_CHUNK : p->k;
+    const uint64_t *nz = (const uint64_t *)(buf + reg[2]);
+    const uint64_t *neg = (const uint64_t *)(buf + reg[3]);
     int bad = 0;
     if (p->value_fmt == OR_TERNARY) {
-        const uint64_t *nz = (const uint64_t *)(buf + reg[2]);
-        const uint64_t *neg = (const uint64_t *)(buf + reg[3]);
+        /* chunks of the last group at or past C: bits C-64(G-1) .. 63 */
+        uint64_t used = C - 64 * (G - 1);
+        uint64_t past = used == 64 ? 0 : ~(((uint64_t)1 << used) - 1);
         for (uint64_t w = 0; w < G * (uint64_t)k; w++) {
             if (neg[w] & ~nz[w])
                 bad = 1;
-            uint64_t g = w / (uint64_t)k;
-            for (uint64_t b = 0; b < 64; b++)
-                if (g * 64 + b >= C && ((nz[w] >> b) & 1u))
-                    bad = 1;
+            if (w / (uint64_t)k == G - 1 && (nz[w] & past))
+                bad = 1;
         }
     }
-    for (uint64_t c = 0; c < C; c++) {
+    uint64_t rows = chunks ? nchunks : C;
+    for (uint64_t i = 0; i < rows; i++) {
+        uint64_t c = chunks ? chunks[i] : i;
+        if (c >= C)
+            return -2;
         for (int s = 0; s < k; s++) {
             uint64_t e = c * (uint64_t)k + (uint64_t)s;
+            uint64_t o = i * (uint64_t)k + (uint64_t)s;
             if (slot_idx)
-                slot_idx[e] = (p->scheme == OR_DCT) ? (int32_t)buf[reg[0] + e] : -1;
+                slot_idx[o] = (p->scheme == OR_DCT) ? (int32_t)buf[reg[0] + e] : -1;
             double v;
             if (p->value_fmt == OR_TERNARY) {
                 uint64_t word = (c / 64) * (uint64_t)k + (uint64_t)s;
                 uint64_t bit = c % 64;
-                const uint64_t *nz = (const uint64_t *)(buf + reg[2]);
-                const uint64_t *neg = (const uint64_t *)(buf + reg[3]);
                 int isnz = (int)((nz[word] >> bit) & 1u);
                 int isneg = (int)((neg[word] >> bit) & 1u);
                 v = isnz ? (isneg ? -1.0 : 1.0) : 0.0;
@@ -677,8 +684,15 @@ int oracle_unpack(const oracle_params *p, uint64_t n_elems, const uint8_t *buf, 
                 v = (double)((const float *)(buf + reg[5]))[e];
             }
             if (slot_val)
-                slot_val[e] = v;
+                slot_val[o] = v;
         }
     }
     return bad ? -1 : 0;
+}
+
+/* inverse of oracle_pack over the whole shard; -1 for a malformed buffer */
+int oracle_unpack(const oracle_params *p, uint64_t n_elems, const uint8_t *buf, int32_t *slot_idx,
+                  double *slot_val)
+{
+    return oracle_unpack_chunks(p, n_elems, buf, NULL, 0, slot_idx, slot_val);
 }

@@ -95,6 +95,51 @@ def test_unpack_flags_malformed_buffers():
     assert not oracle.unpack(p, n, bad)[2]
 
 
+@pytest.mark.parametrize("scheme,k,fmt", [(DCT, 2, TERNARY), (DCT, 3, F16), (RANDOM, 8, F32), (DILOCO, 32, TERNARY)])
+def test_unpack_of_listed_chunks_equals_rows_of_the_whole(scheme, k, fmt):
+    p = Params(scheme=scheme, k=k, value_fmt=fmt, step=15)
+    n = 32 * 64 * 3 + 17  # four groups, a ragged last chunk
+    C = (n + N - 1) // N
+    rng = np.random.default_rng(k)
+    idx, val = _random_slots(C, k, rng, fmt)
+    buf = oracle.pack(p, n, idx, val)
+    i_all, v_all, ok = oracle.unpack(p, n, buf)
+    assert ok
+    ids = np.array([C - 1, 0, 63, 64, 130, 5, 130], np.int64)  # any order, repeats allowed
+    i_s, v_s, ok = oracle.unpack(p, n, buf, chunks=ids)
+    assert ok
+    assert np.array_equal(v_s, v_all[ids]) and np.array_equal(i_s, i_all[ids])
+    with pytest.raises(IndexError):
+        oracle.unpack(p, n, buf, chunks=[C])
+
+
+@pytest.mark.parametrize("C", [10, 64, 129])
+def test_malformed_check_covers_the_whole_buffer(C):
+    """A bit for a chunk past the end, or NEG without NZ, flags the buffer
+    even when the chunks asked for are well formed; a full last group has no
+    chunk past the end."""
+    p = Params(scheme=DCT, k=2)
+    n = 32 * C
+    idx = np.tile(np.array([[1, 4]], np.int32), (C, 1))
+    val = np.ones((C, 2))
+    buf = oracle.pack(p, n, idx, val)
+    reg = oracle.payload_regions(p, n)
+    G = (C + 63) // 64
+    assert oracle.unpack(p, n, buf, chunks=[0])[2]
+    nz = buf[reg["nz_off"]:reg["nz_off"] + reg["plane_bytes"]].view(np.uint64)
+    assert nz[(G - 1) * 2 + 1] == (np.uint64(2**64 - 1) if C % 64 == 0 else np.uint64((1 << (C % 64)) - 1))
+    if C % 64:
+        bad = buf.copy()
+        bad[reg["nz_off"]:reg["nz_off"] + reg["plane_bytes"]].view(np.uint64)[(G - 1) * 2 + 1] |= np.uint64(1 << 63)
+        assert not oracle.unpack(p, n, bad)[2]
+        assert not oracle.unpack(p, n, bad, chunks=[0])[2]
+    bad = buf.copy()
+    w = bad[reg["nz_off"]:reg["nz_off"] + reg["plane_bytes"]].view(np.uint64)
+    w[0] &= ~np.uint64(1 << 3)  # chunk 3, slot 0: NZ cleared, NEG set
+    bad[reg["neg_off"]:reg["neg_off"] + reg["plane_bytes"]].view(np.uint64)[0] |= np.uint64(1 << 3)
+    assert not oracle.unpack(p, n, bad, chunks=[C - 1])[2]
+
+
 def test_f16_conversion_matches_numpy_round_to_nearest_even():
     rng = np.random.default_rng(24)
     xs = np.concatenate([
