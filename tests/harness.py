@@ -219,11 +219,11 @@ class ParityRun:
             u_scale = self.op_scale[r]
             if sends:
                 buf = self.pay[r * self.stride:(r + 1) * self.stride].cpu().numpy()
-                gi, gv, well_formed = oracle.unpack(p, self.n, buf[: self.layout["total_bytes"]])
+                # the sampled chunks' slots; the well-formedness check covers the whole buffer
+                gi, gv, well_formed = oracle.unpack(p, self.n, buf[: self.layout["total_bytes"]],
+                                                    chunks=None if self.full else self.sample)
                 if not well_formed:
                     rep.failures.append(f"replica {r}: malformed payload (NEG without NZ or bits past the end)")
-                gi = gi[self.sample]
-                gv = gv[self.sample]
                 exact = np.all(gv == val_o, axis=1)
                 if p.sign:
                     same = exact.copy()

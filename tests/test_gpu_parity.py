@@ -568,7 +568,11 @@ def _run_full(torch, cfg, segs, R, steps, sample_every, edge, g_std, scales=None
         run.step(t, grads(t))
     print(run.report.summary(), flush=True)
     assert run.report.ok(), run.report.summary()
-    assert run.report.near_ties + run.report.sign_exceptions <= max(3, len(run.sample) // 10000)
+    # every near-tie was checked to be a valid top-k; their number is a sanity
+    # bound (fp32 coefficients reorder gaps of ~1e-7 of the chunk's norm, a few
+    # per million chunk-steps), not part of the acceptance rule
+    exceptions = run.report.near_ties + run.report.sign_exceptions
+    assert exceptions <= 3 + 2e-6 * R * run.report.chunks_checked, run.report.summary()
     del run, m0, th
     torch.cuda.empty_cache()
 
@@ -583,7 +587,8 @@ def test_config3_olmo2_half_shard(torch_cuda, k):
     cfg = L.Config(scheme=L.SCHEME_DCT, k=k)
     segs = synth.olmo2_half_shard()
     scales = synth.layer_scales(0, 18)
-    _run_full(torch_cuda, cfg, segs, 2, 100 if k == 1 else 5, 997, 4096, 1e-3, scales=scales)
+    # every 97th chunk plus the first and last 2^16 chunks, all 100 steps
+    _run_full(torch_cuda, cfg, segs, 2, 100, 97, 1 << 16, 1e-3, scales=scales)
 
 
 @pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
@@ -615,15 +620,18 @@ def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k):
     (L.SCHEME_STRIDE, 8, L.VAL_TERNARY), (L.SCHEME_STRIDE, 16, L.VAL_TERNARY),
 ])
 def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
+    """100 steps with ternary payloads; the fp16 / fp32 value payloads (0.3 to
+    0.6 GB per replica, copied to the host whole every step) run 20."""
     cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt)
     segs = synth.olmo2_half_shard()
-    _run_full(torch_cuda, cfg, segs, 2, 3, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
+    steps = 100 if fmt == L.VAL_TERNARY else 20
+    _run_full(torch_cuda, cfg, segs, 2, steps, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
 
 
 def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda):
     cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
     segs = synth.olmo2_half_shard()
-    _run_full(torch_cuda, cfg, segs, 2, 4, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18),
+    _run_full(torch_cuda, cfg, segs, 2, 20, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18),
               adamw=L.AdamW())
 
 
@@ -699,13 +707,14 @@ def test_olmo2_whole_model_on_one_shard(torch_cuda):
 def test_config4_olmo2_half_shard_diloco(torch_cuda):
     cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16)
     segs = synth.olmo2_half_shard()
-    _run_full(torch_cuda, cfg, segs, 2, 17, 4999, 2048, 1e-3, scales=synth.layer_scales(0, 18))
+    _run_full(torch_cuda, cfg, segs, 2, 100, 4999, 2048, 1e-3, scales=synth.layer_scales(0, 18))
 
 
 @pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
 def test_config5_decode_64_replicas(torch_cuda, scheme, k):
     """Receiver side at R = 64: replica r's payload is the step-0 encode of a
-    state drawn from seed r; the shard then decodes the 64 payloads."""
+    state drawn from seed r; the shard then decodes the 64 payloads in each of
+    50 steps, compared with the oracle after every step."""
     torch = torch_cuda
     segs = synth.olmo2_half_shard()
     n = synth.shard_numel(segs)
@@ -734,16 +743,16 @@ def test_config5_decode_64_replicas(torch_cuda, scheme, k):
         torch.cuda.synchronize()
         peer = oracle.Shard(ids, nvalid, np.zeros((len(sample), 32), np.float32), np.zeros((len(sample), 32), np.float32))
         i_o, v_o, _, _ = peer.encode(p, _chunk_rows(g, n, sample))
-        gi, gv, ok = oracle.unpack(p, n, pay[r * stride:(r + 1) * stride].cpu().numpy())
+        gi, gv, ok = oracle.unpack(p, n, pay[r * stride:(r + 1) * stride].cpu().numpy(), chunks=sample)
         assert ok
-        same = np.all(gv[sample] == v_o, axis=1)
+        same = np.all(gv == v_o, axis=1)
         if scheme == L.SCHEME_DCT:
-            same &= np.all(gi[sample] == i_o, axis=1)
+            same &= np.all(gi == i_o, axis=1)
         assert np.mean(same) > 0.9999, r
         keep = same if r == 0 else keep & same
         idx_l.append(i_o)
         val_l.append(v_o)
-    for t in range(3):
+    for t in range(50):
         cfg.step = 0  # the payloads are step-0 payloads; Random positions use step 0
         L.demo_decode_apply(cfg, n, th, pay, stride, R)
         torch.cuda.synchronize()
