@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+    const uint64_t grp = (uint64_t)xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     uint4* ws = words_all + (VF == VF_TERNARY ? wv * kWave : 0);
     const int k = a.k, R = a.R;
 
-    const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+    const uint64_t grp = (uint64_t)xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    const uint32_t blk = STAGED ? xcd_block(blockIdx.x, gridDim.x) : blockIdx.x;
+    const uint32_t blk = STAGED ? xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) : blockIdx.x;
     const uint64_t grp = (uint64_t)blk * kWavesPerBlock + wv;
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;

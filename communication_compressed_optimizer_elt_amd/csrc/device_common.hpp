@@ -35,15 +35,30 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // Workgroups are handed to the chip's 8 XCDs round-robin by id.  Renumber
-// them so that each XCD takes one contiguous run of ids (XCD x gets
-// ceil or floor of nb/8 of them): payload words that neighbouring groups share
-// in one cache line are then written, or fetched, through one L2 only (the
-// encode measured 2-7% faster, the decode up to 3%).
+// them so that each XCD takes runs of S consecutive ids: block b, the
+// (b / 8)-th block XCD b % 8 receives, goes to run (b / 8) / S of that XCD,
+// and the runs of the 8 XCDs interleave, so the whole chip sweeps the shard
+// front to back while each XCD works on S blocks in a row.  Payload words
+// that neighbouring groups share in one 128-byte line (the 8-byte plane words
+// of 16 groups = 4 blocks at k = 1) are then written, or fetched, through one
+// L2.  Ids past the last whole set of 8*S runs keep their number.
+//
+// The run length is the kernel's: on the OLMo2-1B half shard (639,697,920
+// parameters) the encodes measured fastest with S = 4 (DeMo k = 1: 1.244 ms
+// against 1.302 ms with one contiguous range per XCD; Random n = 8: 1.273
+// against 1.308 ms) and the decodes with S = 16 (0.905 against 0.925 ms;
+// 1.255 against 1.274 ms at R = 64); run lengths that are not powers of two
+// (2, 3, 6, 12, 24) measured slower.
 constexpr uint32_t kXcds = 8;
+constexpr uint32_t kEncodeRun = 4;
+constexpr uint32_t kDecodeRun = 16;
+
+template <uint32_t S>
 __device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nb) {
+    const uint32_t whole = nb - nb % (kXcds * S);
+    if (b >= whole) return b;
     const uint32_t x = b % kXcds, pos = b / kXcds;
-    const uint32_t q = nb / kXcds, rem = nb % kXcds;
-    return x * q + (x < rem ? x : rem) + pos;
+    return ((pos / S) * kXcds + x) * S + pos % S;
 }
 
 __device__ __forceinline__ float sgnf(float x) {

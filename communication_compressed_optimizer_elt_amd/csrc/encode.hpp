@@ -25,7 +25,7 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
     const int k = a.k;
 
     {
-        const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+        const uint64_t grp = (uint64_t)xcd_block<kEncodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
         if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
     const int k = a.k;
 
     {
-        const uint64_t grp = (uint64_t)xcd_block(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+        const uint64_t grp = (uint64_t)xcd_block<kEncodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
         if (grp >= a.G) return;
         const uint64_t base = grp * kGroupElems;
         const bool full = base + kGroupElems <= a.n;
