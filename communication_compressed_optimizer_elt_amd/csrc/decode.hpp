@@ -579,8 +579,7 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    const uint32_t blk = STAGED ? xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) : blockIdx.x;
-    const uint64_t grp = (uint64_t)blk * kWavesPerBlock + wv;
+    const uint64_t grp = (uint64_t)xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
