@@ -102,6 +102,8 @@ def _chunk_rows(t, n, sample):
     import torch
 
     C = (n + CHUNK - 1) // CHUNK
+    if n % CHUNK == 0 and len(sample) == C:  # every chunk, in order (sample is sorted and unique)
+        return t[:n].view(C, CHUNK).cpu().numpy()
     if C * CHUNK >= _GATHER_LIMIT:
         return _chunk_rows_by_runs(t, n, sample)
     if n % CHUNK:

@@ -591,11 +591,13 @@ def test_config3_olmo2_half_shard(torch_cuda, k):
     _run_full(torch_cuda, cfg, segs, 2, 100, 97, 1 << 16, 1e-3, scales=scales)
 
 
-@pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
-def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k):
-    """Step 0 of the OLMo2-1B half shard, R = 2, against the oracle on all
-    19,990,560 chunks and every payload byte: every group of the one-pass
-    grid (XCD-contiguous block numbering included) is checked, not a sample."""
+@pytest.mark.parametrize("scheme,k,steps", [(L.SCHEME_DCT, 1, 3), (L.SCHEME_RANDOM, 8, 1)])
+def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k, steps):
+    """The first steps of the OLMo2-1B half shard, R = 2, against the oracle
+    on all 19,990,560 chunks and every payload byte: every group of the
+    one-pass grid (the per-XCD block numbering included) is checked, not a
+    sample.  DeMo runs steps 0-2, so the momentum read path (zero at step 0)
+    is checked on every chunk too."""
     import time
 
     t0 = time.time()
@@ -606,8 +608,9 @@ def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k):
     assert run.full
     run.set_state(m0, th)
     del m0, th
-    run.step(0, grads(0))
-    print(run.report.summary(), f"{time.time() - t0:.1f} s", flush=True)
+    for t in range(steps):
+        run.step(t, grads(t))
+        print(f"step {t}:", run.report.summary(), f"{time.time() - t0:.1f} s", flush=True)
     assert run.report.ok(), run.report.summary()
     assert run.report.payload_bytes_compared > 0 or run.report.near_ties + run.report.sign_exceptions > 0
     del run
