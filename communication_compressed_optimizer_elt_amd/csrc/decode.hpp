@@ -150,9 +150,14 @@ __device__ __forceinline__ void apply_update(const DecArgs& a, const float* st, 
 }
 
 // The same update with the theta tile loaded up front (prefetch_theta at the
-// start of the kernel, so its latency overlaps the payload work): measured
-// 3-10% faster for the selection and many-entry decodes, neutral for the
-// few-entry DCT decode, which keeps apply_update.
+// start of every decode kernel, so its latency overlaps the payload work), by
+// non-temporal loads: each theta line is read once and then rewritten by the
+// same wave.  On the OLMo2-1B half shard the non-temporal prefetch measured
+// 4-8% faster than plain loads for the R = 2 decodes (DeMo k = 1 0.902 ->
+// 0.850 ms, Random n = 8 0.921 -> 0.863 ms, fp32 values 1.124 -> 1.040 ms)
+// and the R = 64 Random decode (1.436 -> 1.373 ms); a plain-load prefetch was
+// no faster than loading theta after Q in the few-entry DCT decode, and
+// non-temporal loads there after Q were 5% slower.
 struct ThetaTile {
     float4 v[8];
 };
@@ -161,7 +166,7 @@ __device__ __forceinline__ void prefetch_theta(const DecArgs& a, uint64_t base, 
     if (full) {
         const float4* t4 = reinterpret_cast<const float4*>(a.theta + base);
 #pragma unroll
-        for (int r = 0; r < 8; r++) t.v[r] = t4[r * kWave + lane];
+        for (int r = 0; r < 8; r++) t.v[r] = load_stream(t4 + r * kWave + lane);
     }
 }
 
@@ -268,6 +273,8 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     const bool valid = c < a.C;
     const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
 
+    ThetaTile th;  // theta loads go out first
+    prefetch_theta(a, base, full, lane, th);
     float Q[32];
     wave_lds_sync();
 #pragma unroll
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     for (int i = 0; i < 32; i++) Q[i] *= a.invR;
     put_chunk(st, lane, Q);
     wave_lds_sync();
-    apply_update<AD>(a, st, base, full, lane);
+    apply_update_prefetched<AD>(a, st, base, full, lane, th);
 }
 
 // DCT scheme, many entries per chunk: the entries are summed per frequency in
