@@ -111,8 +111,10 @@ constexpr size_t kEncodeLdsReserve = 24 * 1024;
 
 // Decoupled AdamW streams one more array (v) through each kernel.  Its DCT
 // encode (24 KB of loads per wave: g, m, v) measured fastest at 1 block per CU
-// (2.21 ms against 2.31 ms at 2 blocks on a 639,697,920-parameter shard), its
-// decode (v beside theta) at 3 blocks (1.41 ms against 1.42 ms at 4).
+// (2.11 ms against 2.20 ms at 2 blocks on a 639,697,920-parameter shard), its
+// DCT decode (v beside theta) at 3 blocks (1.336 ms against 1.381 ms at 4);
+// its selection decode at the 4 blocks its own LDS allows (1.375 ms against
+// 1.534 ms at 3, Random n = 8), so the reserve applies to the DCT decodes only.
 constexpr size_t kEncodeAdamwLdsReserve = 48 * 1024;
 constexpr size_t kDecodeAdamwLdsReserve = 16 * 1024;
 
@@ -307,7 +309,7 @@ int encode_impl(const demo_cfg* cfg, const demo_adamw* w, uint64_t n_elems, cons
 template <bool AD>
 hipError_t launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block, hipStream_t s) {
     const uint64_t entries = (uint64_t)a.R * (uint64_t)a.k;  // payload entries per chunk
-    const size_t lds = decode_lds_reserve<AD>();
+    const size_t lds = decode_lds_reserve<AD>();  // DCT decodes; the selection decode takes none
     if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
         switch (cfg->value_fmt) {
         case DEMO_VAL_TERNARY: return launch(demo::decode_dct_kernel<demo::VF_TERNARY, AD>, grid, block, lds, s, a);
@@ -325,10 +327,10 @@ hipError_t launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 
     switch (cfg->value_fmt) {
     case DEMO_VAL_TERNARY:
         if (entries > kSelScalarEntries)
-            return launch(demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>, grid, block, lds, s, a);
-        return launch(demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>, grid, block, lds, s, a);
-    case DEMO_VAL_F16: return launch(demo::decode_sel_kernel<demo::VF_F16, false, AD>, grid, block, lds, s, a);
-    default: return launch(demo::decode_sel_kernel<demo::VF_F32, false, AD>, grid, block, lds, s, a);
+            return launch(demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>, grid, block, 0, s, a);
+        return launch(demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>, grid, block, 0, s, a);
+    case DEMO_VAL_F16: return launch(demo::decode_sel_kernel<demo::VF_F16, false, AD>, grid, block, 0, s, a);
+    default: return launch(demo::decode_sel_kernel<demo::VF_F32, false, AD>, grid, block, 0, s, a);
     }
 }
 
