@@ -620,6 +620,7 @@ def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k, 
 @pytest.mark.parametrize("scheme,k,fmt", [
     (L.SCHEME_RANDOM, 8, L.VAL_TERNARY), (L.SCHEME_RANDOM, 16, L.VAL_TERNARY),
     (L.SCHEME_RANDOM, 8, L.VAL_F16), (L.SCHEME_RANDOM, 8, L.VAL_F32),
+    (L.SCHEME_RANDOM, 16, L.VAL_F16), (L.SCHEME_RANDOM, 16, L.VAL_F32),
     (L.SCHEME_STRIDE, 8, L.VAL_TERNARY), (L.SCHEME_STRIDE, 16, L.VAL_TERNARY),
 ])
 def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
