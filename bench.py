@@ -50,9 +50,15 @@ WORKLOADS = {
     "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
     "olmo2-1b-full-demo-k1": ("olmo2-full", "dct", 1, "ternary", 2, "step"),
     "olmo2-1b-half-shard-adamw-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-demo-k1-f32-sign-off": ("olmo2", "dct", 1, "f32", 2, "step"),
+    "olmo2-1b-half-shard-demo-k1-f16-sign-off": ("olmo2", "dct", 1, "f16", 2, "step"),
+    "olmo2-1b-half-shard-random-n8-f16-sign-off": ("olmo2", "random", 8, "f16", 2, "step"),
+    "olmo2-1b-half-shard-random-n8-f32-sign-off": ("olmo2", "random", 8, "f32", 2, "step"),
 }
 # Decoupled AdamW workloads: second moment v read and written by the encode, read by the decode
 ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1"}
+# sign off: the payload slots carry the selected values themselves (DCT coefficients or u)
+SIGN_OFF = {w for w in WORKLOADS if w.endswith("-sign-off")}
 DILOCO_PERIOD = 16
 
 
@@ -122,7 +128,7 @@ def main() -> int:
     g_std = 1e-2 if shard == "vit" else 1e-3
 
     cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, beta=0.9, lr=1e-3, seed=0, step=0,
-                   period=DILOCO_PERIOD)
+                   period=DILOCO_PERIOD, sign=0 if args.workload in SIGN_OFF else 1)
     lay = L.demo_payload_layout(cfg, n)
     stride = lay["total_bytes"]
     payload_bytes = lay["idx_bytes"] + 2 * lay["plane_bytes"] + lay["val_bytes"]
@@ -243,8 +249,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": args.workload, "n_elems": n, "optimizer": "decoupled-adamw" if adamw else "demo-sgd",
-                   "scheme": scheme_name, "k": k,
-                   "value_fmt": fmt_name, "replicas": R, "chunk": 32, "mode": mode},
+                   "scheme": scheme_name, "k": k, "value_fmt": fmt_name, "sign": cfg.sign,
+                   "replicas": R, "chunk": 32, "mode": mode},
         "hbm_gbps": step_gbps,
         "pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "copy_gbps": copy_gbps,
@@ -278,7 +284,8 @@ def cpu_baseline(cfg, n, g, m, theta, peer_grad, R, budget_s):
     zeros = np.zeros((S, 32), np.float32)
     g_rows = g[: S * 32].view(S, 32).cpu().numpy()
     own = oracle.Shard(ids, nv, m[: S * 32].view(S, 32).cpu().numpy(), theta[: S * 32].view(S, 32).cpu().numpy())
-    p = oracle.Params(scheme=cfg.scheme, k=cfg.k, value_fmt=cfg.value_fmt, beta=cfg.beta, lr=cfg.lr, seed=cfg.seed)
+    p = oracle.Params(scheme=cfg.scheme, k=cfg.k, sign=cfg.sign, value_fmt=cfg.value_fmt, beta=cfg.beta, lr=cfg.lr,
+                      seed=cfg.seed)
     peers_idx, peers_val = [], []
     for r in range(1, R):
         peer = oracle.Shard(ids, nv, zeros, zeros)

@@ -632,6 +632,18 @@ def test_config4_olmo2_half_shard_selection_schemes(torch_cuda, scheme, k, fmt):
     _run_full(torch_cuda, cfg, segs, 2, steps, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
 
 
+@pytest.mark.parametrize("scheme,k,fmt", [
+    (L.SCHEME_DCT, 1, L.VAL_F32), (L.SCHEME_DCT, 1, L.VAL_F16),
+    (L.SCHEME_RANDOM, 8, L.VAL_F16), (L.SCHEME_RANDOM, 8, L.VAL_F32),
+])
+def test_olmo2_half_shard_sign_off(torch_cuda, scheme, k, fmt):
+    """Sign off on the OLMo2-1B half shard, R = 2: the payload slots carry the
+    DCT coefficients (or u) as fp32 / fp16 values; 20 steps, sampled chunks."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=0)
+    segs = synth.olmo2_half_shard()
+    _run_full(torch_cuda, cfg, segs, 2, 20, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
+
+
 def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda):
     cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
     segs = synth.olmo2_half_shard()
