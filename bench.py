@@ -50,13 +50,14 @@ WORKLOADS = {
     "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
     "olmo2-1b-full-demo-k1": ("olmo2-full", "dct", 1, "ternary", 2, "step"),
     "olmo2-1b-half-shard-adamw-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
+    "olmo2-1b-half-shard-adamw-random-n8": ("olmo2", "random", 8, "ternary", 2, "step"),
     "olmo2-1b-half-shard-demo-k1-f32-sign-off": ("olmo2", "dct", 1, "f32", 2, "step"),
     "olmo2-1b-half-shard-demo-k1-f16-sign-off": ("olmo2", "dct", 1, "f16", 2, "step"),
     "olmo2-1b-half-shard-random-n8-f16-sign-off": ("olmo2", "random", 8, "f16", 2, "step"),
     "olmo2-1b-half-shard-random-n8-f32-sign-off": ("olmo2", "random", 8, "f32", 2, "step"),
 }
 # Decoupled AdamW workloads: second moment v read and written by the encode, read by the decode
-ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1"}
+ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1", "olmo2-1b-half-shard-adamw-random-n8"}
 # sign off: the payload slots carry the selected values themselves (DCT coefficients or u)
 SIGN_OFF = {w for w in WORKLOADS if w.endswith("-sign-off")}
 DILOCO_PERIOD = 16

@@ -644,8 +644,9 @@ def test_olmo2_half_shard_sign_off(torch_cuda, scheme, k, fmt):
     _run_full(torch_cuda, cfg, segs, 2, 20, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18))
 
 
-def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda):
-    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+@pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
+def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda, scheme, k):
+    cfg = L.Config(scheme=scheme, k=k)
     segs = synth.olmo2_half_shard()
     _run_full(torch_cuda, cfg, segs, 2, 20, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18),
               adamw=L.AdamW())
