@@ -136,6 +136,8 @@ def lib():
         L.oracle_unpack.restype = ctypes.c_int
         L.oracle_unpack_chunks.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P, P, ctypes.c_uint64, P, P]
         L.oracle_unpack_chunks.restype = ctypes.c_int
+        L.oracle_payload_violations.argtypes = [ctypes.POINTER(_Params), ctypes.c_uint64, P]
+        L.oracle_payload_violations.restype = ctypes.c_uint64
         _lib = L
     return _lib
 
@@ -371,3 +373,13 @@ def unpack(p: Params, n_elems: int, buf, chunks=None):
     if r == -2:
         raise IndexError("unpack: chunk id past the shard")
     return idx, val, r == 0
+
+
+def payload_violations(p: Params, n_elems: int, buf) -> int:
+    """Number of violations of the payload format in one replica's buffer
+    (NEG without NZ, bits past the last chunk, index bytes above 31 or not
+    ascending, sign-on values other than -1/0/+1, sign-off non-finite values)."""
+    buf = np.ascontiguousarray(buf, np.uint8)
+    assert buf.size >= payload_regions(p, n_elems)["total_bytes"]
+    c = p.c()
+    return int(lib().oracle_payload_violations(ctypes.byref(c), n_elems, _ptr(buf)))

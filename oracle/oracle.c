@@ -696,3 +696,53 @@ int oracle_unpack(const oracle_params *p, uint64_t n_elems, const uint8_t *buf, 
 {
     return oracle_unpack_chunks(p, n_elems, buf, NULL, 0, slot_idx, slot_val);
 }
+
+/* Violations of the payload format (the statement above and the library
+ * header's), counted one by one over the whole buffer:
+ *  - TERNARY: a NEG bit without its NZ bit, for a chunk c < C;
+ *  - TERNARY: every NZ or NEG bit set for a chunk c >= C (the last group);
+ *  - DCT: an IDX byte above 31;
+ *  - DCT: slot s >= 1 of a chunk whose IDX byte is not above slot s-1's
+ *    (positions must ascend strictly; compared as raw bytes);
+ *  - F16 / F32 with the sign on: a value other than -1, 0 or +1;
+ *  - F16 / F32 with the sign off: a value that is not finite.
+ * A DILOCO step that sends nothing has no payload and no violation. */
+uint64_t oracle_payload_violations(const oracle_params *p, uint64_t n_elems, const uint8_t *buf)
+{
+    if (p->scheme == OR_DILOCO && !is_sync_step(p))
+        return 0;
+    uint64_t reg[8];
+    oracle_payload_regions(p, n_elems, reg);
+    uint64_t C = (n_elems + OR_CHUNK - 1) / OR_CHUNK;
+    uint64_t G = (C + 63) / 64;
+    int k = (p->scheme == OR_DILOCO) ? OR_CHUNK : p->k;
+    uint64_t bad = 0;
+    for (uint64_t c = 0; c < G * 64; c++) {
+        for (int s = 0; s < k; s++) {
+            uint64_t e = c * (uint64_t)k + (uint64_t)s;
+            if (p->value_fmt == OR_TERNARY) {
+                uint64_t word = (c / 64) * (uint64_t)k + (uint64_t)s;
+                int nz = (int)((((const uint64_t *)(buf + reg[2]))[word] >> (c % 64)) & 1u);
+                int ng = (int)((((const uint64_t *)(buf + reg[3]))[word] >> (c % 64)) & 1u);
+                if (c < C)
+                    bad += (uint64_t)(ng && !nz);
+                else
+                    bad += (uint64_t)nz + (uint64_t)ng;
+            } else if (c < C) {
+                double v = (p->value_fmt == OR_F16) ? oracle_from_f16_bits(((const uint16_t *)(buf + reg[5]))[e])
+                                                    : (double)((const float *)(buf + reg[5]))[e];
+                if (p->sign)
+                    bad += (uint64_t)!(v == 0.0 || v == 1.0 || v == -1.0);
+                else
+                    bad += (uint64_t)!isfinite(v);
+            }
+            if (p->scheme == OR_DCT && c < C) {
+                uint8_t b = buf[reg[0] + e];
+                bad += (uint64_t)(b > 31);
+                if (s > 0)
+                    bad += (uint64_t)(b <= buf[reg[0] + e - 1]);
+            }
+        }
+    }
+    return bad;
+}

@@ -152,3 +152,60 @@ def test_f16_conversion_matches_numpy_round_to_nearest_even():
         assert oracle.to_f16_bits(float(x)) == int(h.view(np.uint16)), x
         if np.isfinite(h):
             assert oracle.from_f16_bits(int(h.view(np.uint16))) == float(h)
+
+
+def _region(buf, reg, off_key, nbytes, dtype):
+    return buf[reg[off_key]:reg[off_key] + nbytes].view(dtype)
+
+
+@pytest.mark.parametrize("scheme,k,fmt", [(DCT, 1, TERNARY), (DCT, 3, F16), (RANDOM, 8, F32), (DILOCO, 32, TERNARY)])
+def test_well_formed_payloads_have_no_violations(scheme, k, fmt):
+    p = Params(scheme=scheme, k=k, value_fmt=fmt, step=15)
+    n = 32 * 130 + 9
+    C = (n + N - 1) // N
+    idx, val = _random_slots(C, k, np.random.default_rng(3), fmt)
+    assert oracle.payload_violations(p, n, oracle.pack(p, n, idx, val)) == 0
+
+
+def test_violation_count_on_hand_built_buffers():
+    """Each planted defect counts once: 2 NEG-without-NZ bits, 3 bits past
+    the last chunk, 1 index byte above 31, 1 non-ascending pair."""
+    p = Params(scheme=DCT, k=2)
+    n = 32 * 70  # C = 70: the second group holds chunks 64..69
+    C = 70
+    idx = np.tile(np.array([[3, 9]], np.int32), (C, 1))
+    val = np.ones((C, 2))
+    val[5, 0] = 0.0  # slot 0 of chunk 5 is zero: its NZ bit is clear
+    buf = oracle.pack(p, n, idx, val)
+    reg = oracle.payload_regions(p, n)
+    nz = _region(buf, reg, "nz_off", reg["plane_bytes"], np.uint64)
+    neg = _region(buf, reg, "neg_off", reg["plane_bytes"], np.uint64)
+    neg[0] |= np.uint64(1 << 5)   # chunk 5 slot 0: NEG without NZ
+    neg[1] |= np.uint64(1 << 5)   # chunk 5 slot 1: NZ is set (+1 -> -1), not a violation
+    nz[2] &= ~np.uint64(1 << 1)   # chunk 65 slot 0: NZ cleared ...
+    neg[2] |= np.uint64(1 << 1)   # ... with NEG set: NEG without NZ
+    nz[3] |= np.uint64(1 << 10)   # chunk 74 >= C: one bit past the end
+    nz[2] |= np.uint64(1 << 63)   # chunk 127: past the end
+    neg[2] |= np.uint64(1 << 63)  # and its NEG bit: a second one
+    buf[reg["idx_off"] + 2 * 7] = 40           # chunk 7 slot 0: above 31 (and 40 > 9: a descending pair)
+    buf[reg["idx_off"] + 2 * 8 + 1] = 3        # chunk 8: slots 3, 3 do not ascend
+    assert oracle.payload_violations(p, n, buf) == 2 + 3 + 1 + 1 + 1
+
+
+def test_violation_count_of_value_payloads():
+    n = 32 * 10
+    idx = np.tile(np.array([[0, 1, 2, 3]], np.int32), (10, 1))
+    on = Params(scheme=RANDOM, k=4, value_fmt=F32, sign=1)
+    buf = oracle.pack(on, n, idx, np.ones((10, 4)))
+    reg = oracle.payload_regions(on, n)
+    v = _region(buf, reg, "val_off", reg["val_bytes"], np.float32)
+    v[3], v[7], v[9] = 0.5, -0.0, np.nan  # 0.5 and NaN are not ternary; -0 is zero
+    assert oracle.payload_violations(on, n, buf) == 2
+    off = Params(scheme=RANDOM, k=4, value_fmt=F16, sign=0)
+    buf = oracle.pack(off, n, idx, np.full((10, 4), 0.25))
+    reg = oracle.payload_regions(off, n)
+    h = _region(buf, reg, "val_off", reg["val_bytes"], np.uint16)
+    h[0], h[1], h[2] = 0x7C00, 0x7E00, 0x3555  # +inf and NaN count; a finite value does not
+    assert oracle.payload_violations(off, n, buf) == 2
+    diloco = Params(scheme=DILOCO, period=16, step=3)  # no payload on a non-sync step
+    assert oracle.payload_violations(diloco, n, np.full(1 << 16, 0xFF, np.uint8)) == 0
