@@ -22,7 +22,8 @@ VAL_TERNARY, VAL_F16, VAL_F32 = 0, 1, 2
 OK, EINVAL, EALIGN, EUNSUPPORTED, EHIP, EABI = 0, -1, -2, -3, -4, -5
 
 SYMBOLS = ("demo_abi_version", "demo_strerror", "demo_payload_layout", "demo_encode",
-           "demo_decode_apply", "demo_random_select", "demo_encode_adamw", "demo_decode_apply_adamw")
+           "demo_decode_apply", "demo_random_select", "demo_encode_adamw", "demo_decode_apply_adamw",
+           "demo_payload_validate")
 
 
 class DemoError(RuntimeError):
@@ -129,6 +130,8 @@ def lib() -> ctypes.CDLL:
         L.demo_decode_apply_adamw.argtypes = [ctypes.POINTER(demo_cfg), ctypes.POINTER(demo_adamw),
                                               ctypes.c_uint64, P, P, P, ctypes.c_uint64, ctypes.c_uint32, P]
         L.demo_decode_apply_adamw.restype = ctypes.c_int
+        L.demo_payload_validate.argtypes = [ctypes.POINTER(demo_cfg), ctypes.c_uint64, P, P, P]
+        L.demo_payload_validate.restype = ctypes.c_int
         if L.demo_abi_version() != ABI_VERSION:
             raise RuntimeError("libdemo.so ABI version mismatch")
         _lib = L
@@ -234,6 +237,16 @@ def demo_random_select(cfg, seed: int, step: int, n_chunks: int, masks_out, stre
                                     _stream(stream)), "demo_random_select")
 
 
+def demo_payload_validate(cfg, n_elems: int, payload, violations_out, stream=None) -> None:
+    """violations_out: device int64 tensor of at least one element; the count
+    is written asynchronously on the stream."""
+    c = _cfg(cfg)
+    pb = _payload_bytes(c, n_elems) if _sends(c) else 0
+    _check(lib().demo_payload_validate(ctypes.byref(c), n_elems, _buf(payload, "payload", pb),
+                                       _buf(violations_out, "violations_out", 8, elem=8), _stream(stream)),
+           "demo_payload_validate")
+
+
 def demo_encode_adamw(cfg, adamw, n_elems: int, grad, moment1, moment2, payload_out, q_out=None,
                       stream=None) -> None:
     c = _cfg(cfg)
@@ -295,3 +308,8 @@ def raw_decode_apply_adamw(cfg, adamw, n_elems, params, moment2, payloads, strid
     wp = None if adamw is None else ctypes.byref(w)
     return int(lib().demo_decode_apply_adamw(ctypes.byref(c), wp, n_elems, params, moment2, payloads, stride, R,
                                              stream))
+
+
+def raw_payload_validate(cfg, n_elems, payload, violations_out, stream=0) -> int:
+    c = _cfg(cfg)
+    return int(lib().demo_payload_validate(ctypes.byref(c), n_elems, payload, violations_out, stream))

@@ -678,6 +678,60 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
 
 // ------------------------------------------------------------------ select --
 
+// ------------------------------------------------------------- validation --
+
+// Payload check for a receiver (demo_payload_validate): one wave per group of
+// 64 chunks, lane = chunk; every violation of the format counts once:
+// a NEG bit without its NZ bit (chunks < C), any NZ / NEG bit of a chunk >= C,
+// an IDX byte above 31 or not above the previous slot's, a sign-on value other
+// than -1 / 0 / +1, a sign-off value that is not finite.  The wave's total is
+// added to *out (cleared beforehand by zero_u64_kernel).
+struct CheckArgs {
+    const uint8_t* pay;
+    unsigned long long* out;
+    uint64_t C, G;
+    uint64_t idx_off, nz_off, neg_off, val_off;
+    int k;
+    int dct;
+    int sign;
+};
+
+template <int VF>
+__global__ __launch_bounds__(kBlock) void validate_kernel(CheckArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint64_t grp = (uint64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave;
+    if (grp >= a.G) return;
+    const uint64_t c = grp * kWave + lane;
+    const bool valid = c < a.C;
+    uint32_t bad = 0;
+    int prev = -1;
+    for (int s = 0; s < a.k; s++) {
+        const uint64_t e = c * (uint64_t)a.k + (uint64_t)s;
+        if (VF == VF_TERNARY) {
+            const uint64_t w = grp * (uint64_t)a.k + (uint64_t)s;
+            const bool nz = (reinterpret_cast<const uint64_t*>(a.pay + a.nz_off)[w] >> lane) & 1ull;
+            const bool ng = (reinterpret_cast<const uint64_t*>(a.pay + a.neg_off)[w] >> lane) & 1ull;
+            bad += valid ? (uint32_t)(ng && !nz) : (uint32_t)nz + (uint32_t)ng;
+        } else if (valid) {
+            const float v = VF == VF_F32 ? reinterpret_cast<const float*>(a.pay + a.val_off)[e]
+                                         : __half2float(__ushort_as_half(
+                                               reinterpret_cast<const uint16_t*>(a.pay + a.val_off)[e]));
+            bad += a.sign ? (uint32_t)!(v == 0.f || v == 1.f || v == -1.f) : (uint32_t)!isfinite(v);
+        }
+        if (a.dct && valid) {
+            const int b = a.pay[a.idx_off + e];
+            bad += (uint32_t)(b > 31) + (uint32_t)(b <= prev);
+            prev = b;
+        }
+    }
+    unsigned long long total = bad;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) total += __shfl_xor(total, d);
+    if (lane == 0 && total) atomicAdd(a.out, total);
+}
+
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+
 __global__ __launch_bounds__(256) void select_kernel(uint32_t* out, uint64_t n_chunks, uint64_t chunk_offset,
                                                      uint64_t seed, uint32_t step_lo, int k, int random,
                                                      uint32_t mask) {

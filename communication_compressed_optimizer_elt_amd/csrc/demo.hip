@@ -417,6 +417,43 @@ int demo_decode_apply_adamw(const demo_cfg* cfg, const demo_adamw* adamw, uint64
     return decode_impl(cfg, adamw, n_elems, params, moment2, payloads, stride, R, hip_stream);
 }
 
+int demo_payload_validate(const demo_cfg* cfg, uint64_t n_elems, const void* payload, uint64_t* violations_out,
+                          void* hip_stream) {
+    int rc = check_cfg(cfg);
+    if (rc) return rc;
+    if ((rc = check_size(cfg, n_elems))) return rc;
+    const bool sends = cfg->scheme != DEMO_SCHEME_DILOCO || is_sync_step(cfg);
+    if (!violations_out || (sends && !payload)) return DEMO_EINVAL;
+    if (((uintptr_t)violations_out & 7u) != 0 || (sends && !aligned16(payload))) return DEMO_EALIGN;
+    demo_layout L;
+    layout_of(cfg, n_elems, &L);
+    if (sends && overlap(payload, L.total_bytes, violations_out, 8)) return DEMO_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    unsigned long long* out = reinterpret_cast<unsigned long long*>(violations_out);
+    // cleared by a kernel rather than a memset, so the call can be captured in a HIP graph
+    hipError_t e = launch(demo::zero_u64_kernel, dim3(1), dim3(1), 0, s, out);
+    if (e != hipSuccess || !sends) return status_of(e);
+    const uint64_t C = (n_elems + 31) / 32;
+    demo::CheckArgs a{};
+    a.pay = static_cast<const uint8_t*>(payload);
+    a.out = out;
+    a.C = C;
+    a.G = (C + 63) / 64;
+    a.idx_off = L.idx_off;
+    a.nz_off = L.nz_off;
+    a.neg_off = L.neg_off;
+    a.val_off = L.val_off;
+    a.k = slots_per_chunk(cfg);
+    a.dct = cfg->scheme == DEMO_SCHEME_DCT;
+    a.sign = (int)cfg->sign;
+    const dim3 grid(grid_for_groups(a.G)), block(demo::kBlock);
+    switch (cfg->value_fmt) {
+    case DEMO_VAL_TERNARY: return status_of(launch(demo::validate_kernel<demo::VF_TERNARY>, grid, block, 0, s, a));
+    case DEMO_VAL_F16: return status_of(launch(demo::validate_kernel<demo::VF_F16>, grid, block, 0, s, a));
+    default: return status_of(launch(demo::validate_kernel<demo::VF_F32>, grid, block, 0, s, a));
+    }
+}
+
 int demo_random_select(const demo_cfg* cfg, uint64_t seed, uint64_t step, uint64_t n_chunks, uint32_t* masks_out,
                        void* hip_stream) {
     int rc = check_cfg(cfg);

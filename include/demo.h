@@ -197,6 +197,25 @@ int demo_decode_apply_adamw(const demo_cfg *cfg, const demo_adamw *adamw, uint64
                             void *hip_stream);
 
 /*
+ * Receiver-side check of one replica's payload before demo_decode_apply: the
+ * payload comes from another replica (the exchange of Algorithm 1 step 6 in
+ * the DeToNATION notes), and this call counts, into *violations_out, every
+ * violation of the format stated at demo_layout for this cfg and n_elems:
+ * a NEG bit without its NZ bit (chunks c < C); each NZ or NEG bit of a chunk
+ * c >= C; an IDX byte above 31; an IDX byte not above the previous slot's
+ * (positions must ascend strictly); with cfg->sign 1 an F16/F32 value other
+ * than -1, 0 or +1 (the ternary values of sign before sync); with cfg->sign 0
+ * a value that is not finite.  0 means well formed.  A DILOCO step that sends
+ * nothing has no payload: payload may be NULL and the count is 0.
+ * payload: device buffer of at least demo_payload_layout's total_bytes,
+ * 16-byte aligned, read-only.  violations_out: device uint64, 8-byte aligned,
+ * written asynchronously on hip_stream (read it after synchronising); it must
+ * not overlap the payload.  The count is cleared by a kernel, not a memset.
+ */
+int demo_payload_validate(const demo_cfg *cfg, uint64_t n_elems, const void *payload, uint64_t *violations_out,
+                          void *hip_stream);
+
+/*
  * Shared-seed slot positions of n_chunks chunks (global ids chunk_offset +
  * c, c < n_chunks): masks_out[c] bit j set iff chunk-local position j is
  * selected.  cfg->scheme RANDOM: k positions drawn without replacement by

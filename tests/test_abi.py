@@ -119,6 +119,21 @@ def test_select_validation(lib):
     assert L.raw_random_select(_cfg(scheme=L.SCHEME_RANDOM, k=8), 0, 0, 10, A + 2) == L.EALIGN
 
 
+def test_validate_validation(lib):
+    """demo_payload_validate rejects bad arguments before launching anything."""
+    cfg = _cfg(k=2)
+    assert L.raw_payload_validate(_cfg(k=0), 1024, A, 2 * A) == L.EINVAL
+    assert L.raw_payload_validate(_cfg(abi_version=7), 1024, A, 2 * A) == L.EABI
+    assert L.raw_payload_validate(cfg, 0, A, 2 * A) == L.EINVAL
+    assert L.raw_payload_validate(cfg, 1024, None, 2 * A) == L.EINVAL
+    assert L.raw_payload_validate(cfg, 1024, A, None) == L.EINVAL
+    assert L.raw_payload_validate(cfg, 1024, A + 8, 2 * A) == L.EALIGN
+    assert L.raw_payload_validate(cfg, 1024, A, 2 * A + 4) == L.EALIGN
+    assert L.raw_payload_validate(cfg, 1024, A, A + 8) == L.EINVAL  # the count inside the payload
+    # a DiLoCo sync step needs a payload
+    assert L.raw_payload_validate(_cfg(scheme=L.SCHEME_DILOCO, period=16, step=15), 1024, None, 2 * A) == L.EINVAL
+
+
 def test_diloco_non_sync_step_needs_no_payload(lib):
     # no payload is written on a non-sync step, so NULL is accepted for it ...
     cfg = _cfg(scheme=L.SCHEME_DILOCO, period=16, step=3)

@@ -537,6 +537,130 @@ def test_decode_reads_stray_bits_as_the_format_says(torch_cuda, scheme, k, R):
     assert not torch.equal(clean_th, th0)
 
 
+# ------------------------------------------------------ payload validation --
+
+def _encoded_payload(torch, cfg, n, seed=0):
+    """One replica's payload from demo_encode of a seeded state (host copy too)."""
+    lay = L.demo_payload_layout(cfg, n)
+    pay = torch.zeros(lay["total_bytes"], dtype=torch.uint8, device="cuda")
+    g = torch.from_numpy(synth.normal_np(n, 1.0, seed, synth.TAG_GRAD)).cuda()
+    m = torch.from_numpy(synth.normal_np(n, 1.0, seed, synth.TAG_MOM)).cuda()
+    L.demo_encode(cfg, n, g, m, pay)
+    torch.cuda.synchronize()
+    return pay
+
+
+def _gpu_violations(torch, cfg, n, pay, out=None):
+    out = torch.full((1,), 12345, dtype=torch.int64, device="cuda") if out is None else out
+    L.demo_payload_validate(cfg, n, pay, out)
+    torch.cuda.synchronize()
+    return int(out.item())
+
+
+@pytest.mark.parametrize("scheme,k,fmt,sign", [
+    (L.SCHEME_DCT, 1, L.VAL_TERNARY, 1), (L.SCHEME_DCT, 3, L.VAL_TERNARY, 1), (L.SCHEME_DCT, 12, L.VAL_F16, 1),
+    (L.SCHEME_DCT, 2, L.VAL_F32, 0), (L.SCHEME_DCT, 4, L.VAL_F16, 0), (L.SCHEME_RANDOM, 8, L.VAL_TERNARY, 1),
+    (L.SCHEME_RANDOM, 16, L.VAL_F32, 1), (L.SCHEME_STRIDE, 4, L.VAL_F16, 0), (L.SCHEME_DILOCO, 32, L.VAL_TERNARY, 1),
+])
+@pytest.mark.parametrize("n", [7, 32 * 64 * 5 + 40])
+def test_payload_validate_counts_what_the_oracle_counts(torch_cuda, scheme, k, fmt, sign, n):
+    """A payload written by demo_encode has no violation; after seeded random
+    byte corruption the GPU count equals the oracle's count exactly."""
+    torch = torch_cuda
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=sign, period=16, step=15)
+    p = oracle_params(cfg)
+    pay = _encoded_payload(torch, cfg, n)
+    host = pay.cpu().numpy()
+    assert _gpu_violations(torch, cfg, n, pay) == 0 == oracle.payload_violations(p, n, host)
+    rng = np.random.default_rng(n + 97 * k + 7 * fmt + sign)
+    total = int(L.demo_payload_layout(cfg, n)["total_bytes"])
+    for trial in range(3):
+        bad = host.copy()
+        pos = rng.integers(0, total, size=1 + trial * 40)
+        bad[pos] = rng.integers(0, 256, size=pos.size).astype(np.uint8)
+        want = oracle.payload_violations(p, n, bad)
+        got = _gpu_violations(torch, cfg, n, torch.from_numpy(bad).cuda())
+        assert got == want, (trial, got, want)
+
+
+def test_payload_validate_edge_cases(torch_cuda):
+    """A DiLoCo step without a payload counts 0 (the count is cleared even
+    with no payload); repeated calls on one count buffer do not accumulate."""
+    torch = torch_cuda
+    n = 4099
+    out = torch.full((1,), 777, dtype=torch.int64, device="cuda")
+    quiet = L.Config(scheme=L.SCHEME_DILOCO, period=16, step=3)
+    assert _gpu_violations(torch, quiet, n, None, out) == 0
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=2)
+    pay = _encoded_payload(torch, cfg, n)
+    lay = L.demo_payload_layout(cfg, n)
+    bad = pay.clone()
+    bad[lay["idx_off"] + 5] = 200  # chunk 2 slot 1: above 31 (and not below slot 0's byte: ascending)
+    want = oracle.payload_violations(oracle_params(cfg), n, bad.cpu().numpy())
+    assert want >= 1
+    assert _gpu_violations(torch, cfg, n, bad, out) == want
+    assert _gpu_violations(torch, cfg, n, bad, out) == want
+    assert _gpu_violations(torch, cfg, n, pay, out) == 0
+
+
+def test_payload_validate_on_the_olmo2_half_shard(torch_cuda):
+    """The R = 2 DeMo k = 1 payload of the OLMo2-1B half shard (19,990,560
+    chunks) is well formed; planted defects are counted exactly."""
+    torch = torch_cuda
+    segs = synth.olmo2_half_shard()
+    n = synth.shard_numel(segs)
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1)
+    lay = L.demo_payload_layout(cfg, n)
+    pay = torch.zeros(lay["total_bytes"], dtype=torch.uint8, device="cuda")
+    g = synth.scaled_grad_torch(segs, synth.layer_scales(0, 18), 1e-3, 0, 0)
+    m = torch.zeros_like(g)
+    L.demo_encode(cfg, n, g, m, pay)
+    torch.cuda.synchronize()
+    del g, m
+    assert _gpu_violations(torch, cfg, n, pay) == 0
+    C = n // 32
+    pay[lay["idx_off"] + C - 1] = 32                      # last chunk's index above 31
+    nz = pay[lay["nz_off"]:lay["nz_off"] + lay["plane_bytes"]].view(torch.int64)
+    neg = pay[lay["neg_off"]:lay["neg_off"] + lay["plane_bytes"]].view(torch.int64)
+    neg[1000] = neg[1000] | (~nz[1000] & 0xF)              # NEG without NZ in the low 4 chunks of group 1000
+    planted = 1 + int(bin(int((~nz[1000] & 0xF).item()) & 0xF).count("1"))
+    assert _gpu_violations(torch, cfg, n, pay) == planted
+    host = pay.cpu().numpy()
+    assert oracle.payload_violations(oracle_params(cfg), n, host) == planted
+    torch.cuda.empty_cache()
+
+
+def test_payload_validate_in_a_hip_graph(torch_cuda):
+    """demo_payload_validate captured in a HIP graph (the count is cleared by a
+    kernel, no memset) and replayed with the payload changed eagerly between
+    replays: every replay counts the payload as it is then."""
+    torch = torch_cuda
+    n = 32 * 64 * 3 + 9
+    cfg = L.Config(scheme=L.SCHEME_RANDOM, k=8)
+    pay = _encoded_payload(torch, cfg, n)
+    clean = pay.clone()
+    lay = L.demo_payload_layout(cfg, n)
+    out = torch.zeros(1, dtype=torch.int64, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        L.demo_payload_validate(cfg, n, pay, out, s)
+    torch.cuda.synchronize()
+    p = oracle_params(cfg)
+    G = (n // 32 + 1 + 63) // 64  # 193 chunks: the last group holds chunk 192 only
+    for i in range(4):
+        pay.copy_(clean)
+        if i % 2:  # NZ bits of chunks 248..255 (past the end) in slot i of the last group
+            pay[lay["nz_off"] + ((G - 1) * 8 + i) * 8 + 7] = 0xFF
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        want = oracle.payload_violations(p, n, pay.cpu().numpy())
+        assert int(out.item()) == want, (i, int(out.item()), want)
+        assert want == (8 if i % 2 else 0)
+
+
 # --------------------------------------------------------- full-size shards --
 
 def _sample(C, every, edge):
