@@ -24,6 +24,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 CHUNK = 32
 DCT, RANDOM, STRIDE, DILOCO = 0, 1, 2, 3
 TERNARY, F16, F32 = 0, 1, 2
+# guided encode: bits of the per-chunk status
+GUIDE_POSITIONS, GUIDE_SIGNS, GUIDE_REJECTED = 1, 2, 4
 
 
 def build(force: bool = False) -> str:
@@ -118,13 +120,14 @@ def lib():
         L.oracle_from_f16_bits.restype = ctypes.c_double
         L.oracle_wire_value.argtypes = [ctypes.POINTER(_Params), ctypes.c_double]
         L.oracle_wire_value.restype = ctypes.c_double
-        L.oracle_encode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, P, P, P, P, P, P]
+        L.oracle_encode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, P, P, P, P, P, P,
+                                    P, P, ctypes.c_double, P]
         L.oracle_encode.restype = ctypes.c_int
         L.oracle_decode.argtypes = [ctypes.POINTER(_Params), ctypes.c_int64, P, P, ctypes.c_int32,
                                     P, P, P, P]
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_encode_adamw.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_AdamW), ctypes.c_int64,
-                                          P, P, P, P, P, P, P, P, P]
+                                          P, P, P, P, P, P, P, P, P, P, P, ctypes.c_double, P]
         L.oracle_encode_adamw.restype = ctypes.c_int
         L.oracle_decode_adamw.argtypes = [ctypes.POINTER(_Params), ctypes.POINTER(_AdamW), ctypes.c_int64,
                                           P, P, ctypes.c_int32, P, P, P, P, P]
@@ -268,6 +271,24 @@ class Shard:
     def encode(self, p: Params, g, adamw: AdamW | None = None):
         """Algorithm 1 steps 3-5 (Decoupled AdamW's moments when adamw is
         given). g is fp32 [n][32]. Returns (idx, val, q, X)."""
+        return self._encode(p, g, adamw, None, None, 0.0)[:4]
+
+    def encode_guided(self, p: Params, g, guide_idx, guide_val, near: float, adamw: AdamW | None = None):
+        """encode, taking another implementation's positions (DCT) and ternary
+        signs where several are correct: a guide that is a valid top-k up to
+        near * max|X|, or a sign of a value within near * max|x| of zero.
+        guide_idx / guide_val are [n][slots] as encode returns them.  Returns
+        (idx, val, q, X, status) with status [n] the GUIDE_* bits per chunk
+        (GUIDE_REJECTED: the guide differs where only one answer is right;
+        the oracle then keeps its own)."""
+        s = slots(p)
+        gi = np.ascontiguousarray(np.asarray(guide_idx, np.int32).reshape(self.n, s) if s else
+                                  np.zeros((self.n, 1), np.int32))
+        gv = np.ascontiguousarray(np.asarray(guide_val, np.float64).reshape(self.n, s) if s else
+                                  np.zeros((self.n, 1), np.float64))
+        return self._encode(p, g, adamw, gi, gv, near)
+
+    def _encode(self, p, g, adamw, gi, gv, near):
         n = self.n
         g = np.ascontiguousarray(np.asarray(g, np.float32).reshape(n, CHUNK))
         s = slots(p)
@@ -275,18 +296,21 @@ class Shard:
         val = np.zeros((n, max(s, 1)), np.float64)
         q = np.zeros((n, CHUNK), np.float64)
         X = np.zeros((n, CHUNK), np.float64)
+        status = np.zeros(n, np.int32)
+        st = None if gi is None else status
         c = p.c()
         if adamw is None:
             r = lib().oracle_encode(ctypes.byref(c), n, _ptr(self.chunk_ids), _ptr(self.nvalid), _ptr(g),
-                                    _ptr(self.m), _ptr(idx), _ptr(val), _ptr(q), _ptr(X))
+                                    _ptr(self.m), _ptr(idx), _ptr(val), _ptr(q), _ptr(X), _ptr(gi), _ptr(gv),
+                                    float(near), _ptr(st))
         else:
             w = adamw.c()
             r = lib().oracle_encode_adamw(ctypes.byref(c), ctypes.byref(w), n, _ptr(self.chunk_ids),
                                           _ptr(self.nvalid), _ptr(g), _ptr(self.m), _ptr(self.v), _ptr(idx),
-                                          _ptr(val), _ptr(q), _ptr(X))
+                                          _ptr(val), _ptr(q), _ptr(X), _ptr(gi), _ptr(gv), float(near), _ptr(st))
         if r < 0:
             raise ValueError("oracle_encode: bad configuration")
-        return idx[:, :s], val[:, :s], q, X
+        return idx[:, :s], val[:, :s], q, X, status
 
     def decode(self, p: Params, idx_list, val_list, adamw: AdamW | None = None):
         """Algorithm 1 steps 6-7 over R payloads (own first); with adamw the

@@ -33,6 +33,11 @@
  *  - top-k keeps the k largest |X_j|; equal magnitudes go to the lower index.
  *    The comparison is taken on |X_j| rounded to fp32, the precision the GPU
  *    decides in (the pages fix none); slots are emitted in ascending index.
+ *  - several selections are correct where the k-th and (k+1)-th |X_j| lie
+ *    within a rounding of each other, and a sign is open where the selected
+ *    value lies within a rounding of 0: the guided encode below takes another
+ *    implementation's choice in exactly those cases (and rejects it in every
+ *    other), so the two trajectories stay comparable.
  *  - q uses the unsigned coefficients; only the payload carries signs.
  *  - sign(0) = 0; the aggregate is the plain mean over all R payloads
  *    (own included) with no second sign.
@@ -48,7 +53,10 @@
  *    momentum's place in extraction and error feedback; v = beta2*v +
  *    (1-beta2)*g^2; the exchanged Q is applied as AdamW applies its first
  *    moment: theta -= eta*((Q/(1-beta1^t)) / (sqrt(v/(1-beta2^t)) + eps)
- *    + wd*theta), t = step + 1.
+ *    + wd*theta), t = step + 1.  The slots carry the values themselves (sign
+ *    off): a ternary Q has already lost the first moment's magnitude, and
+ *    dividing it by sqrt(v) would scale the step by 1/|g| (a sign-on
+ *    configuration is rejected).
  */
 #include <math.h>
 #include <omp.h>
@@ -354,6 +362,47 @@ double oracle_wire_value(const oracle_params *p, double x)
 }
 
 /* ------------------------------------------------------------------------ */
+/* Guide: where more than one result is correct, take the one another        */
+/* implementation chose, and only there.                                     */
+/*  - positions (DCT): the guide's k positions must be distinct, ascending   */
+/*    and in [0, 32), and every guided |X_j| must be at least every unguided */
+/*    |X_j| less near * max_j |X_j| (fp64 coefficients): then they are a     */
+/*    valid top-k up to rounding and are adopted (GUIDE_POSITIONS);          */
+/*  - signs (sign before sync): a slot whose guided ternary value differs    */
+/*    from sign(x) is adopted if |x| <= near * max_j |x_j| (x = X for DCT,   */
+/*    u otherwise; GUIDE_SIGNS);                                             */
+/*  - anything else that differs is GUIDE_REJECTED and the oracle keeps its  */
+/*    own choice.  Values with the sign off are not guided.                  */
+/* ------------------------------------------------------------------------ */
+
+enum { OR_GUIDE_POSITIONS = 1, OR_GUIDE_SIGNS = 2, OR_GUIDE_REJECTED = 4 };
+
+static int guide_is_near_topk(const double *X, const int32_t *gidx, int k, double near)
+{
+    uint32_t in = 0;
+    for (int s = 0; s < k; s++) {
+        if (gidx[s] < 0 || gidx[s] >= OR_CHUNK)
+            return 0;
+        if (s > 0 && gidx[s] <= gidx[s - 1])
+            return 0;
+        in |= 1u << gidx[s];
+    }
+    double top = 0.0, min_in = INFINITY, max_out = 0.0;
+    for (int j = 0; j < OR_CHUNK; j++) {
+        double a = fabs(X[j]);
+        if (a > top)
+            top = a;
+        if (in & (1u << j)) {
+            if (a < min_in)
+                min_in = a;
+        } else if (a > max_out) {
+            max_out = a;
+        }
+    }
+    return min_in >= max_out - near * top;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Encode: Algorithm 1 steps 3-5 for a list of chunks.                       */
 /*   g      : fp32 gradients, [n][32], padded positions ignored              */
 /*   m      : fp64 momentum state, [n][32], updated in place (pads kept 0)   */
@@ -364,12 +413,16 @@ double oracle_wire_value(const oracle_params *p, double x)
 /*   slot_val [n][slots] the value the slot carries on the wire              */
 /*   q_out    [n][32]    extracted component q                               */
 /*   x_out    [n][32]    DCT coefficients (DCT scheme) or u (others)         */
+/* Guide (all NULL for a plain encode): guide_idx / guide_val [n][slots] in   */
+/* the layout of slot_idx / slot_val, tolerance near, and guide_status [n]    */
+/* receiving the OR_GUIDE_* bits of each chunk (0: nothing differed).         */
 /* Returns slots per chunk, or -1 on a bad configuration.                    */
 /* ------------------------------------------------------------------------ */
 
 static int encode_impl(const oracle_params *p, double gamma, int64_t n, const uint64_t *chunk_id,
                        const int32_t *nvalid, const float *g, double *m, int32_t *slot_idx, double *slot_val,
-                       double *q_out, double *x_out)
+                       double *q_out, double *x_out, const int32_t *guide_idx, const double *guide_val,
+                       double near, int32_t *guide_status)
 {
     if (p->scheme < OR_DCT || p->scheme > OR_DILOCO)
         return -1;
@@ -380,6 +433,7 @@ static int encode_impl(const oracle_params *p, double gamma, int64_t n, const ui
     if (p->scheme == OR_DILOCO && p->period < 1)
         return -1;
     const int slots = oracle_slots(p);
+    const int guided = guide_idx != NULL && guide_val != NULL;
     const double beta = (double)p->beta;
     double B[OR_CHUNK * OR_CHUNK];
     oracle_basis(B);
@@ -392,6 +446,8 @@ static int encode_impl(const oracle_params *p, double gamma, int64_t n, const ui
         double u[OR_CHUNK], q[OR_CHUNK], X[OR_CHUNK];
         int32_t sel[OR_CHUNK];
         double val[OR_CHUNK];
+        double raw[OR_CHUNK]; /* the selected value of each slot, before the wire */
+        int status = 0;
 
         /* step 3: momentum accumulation (pads are zero); gamma = 1, or 1 - beta1
          * for the AdamW first moment */
@@ -405,11 +461,26 @@ static int encode_impl(const oracle_params *p, double gamma, int64_t n, const ui
             double Xs[OR_CHUNK];
             dct_with(B, u, X);
             oracle_topk(X, p->k, sel);
+            if (guided) {
+                const int32_t *gs = guide_idx + c * slots;
+                int differs = 0;
+                for (int s = 0; s < slots; s++)
+                    differs |= gs[s] != sel[s];
+                if (differs) {
+                    if (guide_is_near_topk(X, gs, slots, near)) {
+                        for (int s = 0; s < slots; s++)
+                            sel[s] = gs[s];
+                        status |= OR_GUIDE_POSITIONS;
+                    } else {
+                        status |= OR_GUIDE_REJECTED;
+                    }
+                }
+            }
             for (int j = 0; j < OR_CHUNK; j++)
                 Xs[j] = 0.0;
             for (int s = 0; s < slots; s++) {
                 Xs[sel[s]] = X[sel[s]];
-                val[s] = oracle_wire_value(p, X[sel[s]]);
+                raw[s] = X[sel[s]];
             }
             idct_with(B, Xs, q);
         } else {
@@ -420,8 +491,28 @@ static int encode_impl(const oracle_params *p, double gamma, int64_t n, const ui
                 if (mask & (1u << j)) {
                     q[j] = u[j];
                     sel[s] = j;
-                    val[s] = oracle_wire_value(p, u[j]);
+                    raw[s] = u[j];
                     s++;
+                }
+            }
+        }
+        for (int s = 0; s < slots; s++)
+            val[s] = oracle_wire_value(p, raw[s]);
+        if (guided && p->sign) {
+            const double *gv = guide_val + c * slots;
+            double top = 0.0;
+            for (int j = 0; j < OR_CHUNK; j++)
+                if (fabs(X[j]) > top)
+                    top = fabs(X[j]);
+            for (int s = 0; s < slots; s++) {
+                if (gv[s] == val[s])
+                    continue;
+                int ternary = gv[s] == 1.0 || gv[s] == -1.0 || gv[s] == 0.0;
+                if (ternary && fabs(raw[s]) <= near * top) {
+                    val[s] = gv[s];
+                    status |= OR_GUIDE_SIGNS;
+                } else {
+                    status |= OR_GUIDE_REJECTED;
                 }
             }
         }
@@ -442,23 +533,30 @@ static int encode_impl(const oracle_params *p, double gamma, int64_t n, const ui
         if (x_out)
             for (int i = 0; i < OR_CHUNK; i++)
                 x_out[c * OR_CHUNK + i] = X[i];
+        if (guide_status)
+            guide_status[c] = status;
     }
     return slots;
 }
 
 int oracle_encode(const oracle_params *p, int64_t n, const uint64_t *chunk_id, const int32_t *nvalid,
                   const float *g, double *m, int32_t *slot_idx, double *slot_val, double *q_out,
-                  double *x_out)
+                  double *x_out, const int32_t *guide_idx, const double *guide_val, double near,
+                  int32_t *guide_status)
 {
-    return encode_impl(p, 1.0, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out);
+    return encode_impl(p, 1.0, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out, guide_idx, guide_val,
+                       near, guide_status);
 }
 
 /* Decoupled AdamW encode: the second moment v (fp64, [n][32], pads kept 0)
  * takes g^2; the first moment m then goes through the same steps 3-5. */
 int oracle_encode_adamw(const oracle_params *p, const oracle_adamw *w, int64_t n, const uint64_t *chunk_id,
                         const int32_t *nvalid, const float *g, double *m, double *v, int32_t *slot_idx,
-                        double *slot_val, double *q_out, double *x_out)
+                        double *slot_val, double *q_out, double *x_out, const int32_t *guide_idx,
+                        const double *guide_val, double near, int32_t *guide_status)
 {
+    if (p->sign)
+        return -1;
     const double beta2 = (double)w->beta2;
 #pragma omp parallel for schedule(static)
     for (int64_t c = 0; c < n; c++)
@@ -466,7 +564,8 @@ int oracle_encode_adamw(const oracle_params *p, const oracle_adamw *w, int64_t n
             const double gi = (double)g[c * OR_CHUNK + i];
             v[c * OR_CHUNK + i] = (i < nvalid[c]) ? beta2 * v[c * OR_CHUNK + i] + (1.0 - beta2) * gi * gi : 0.0;
         }
-    return encode_impl(p, 1.0 - (double)p->beta, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out);
+    return encode_impl(p, 1.0 - (double)p->beta, n, chunk_id, nvalid, g, m, slot_idx, slot_val, q_out, x_out,
+                       guide_idx, guide_val, near, guide_status);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -553,6 +652,8 @@ int oracle_decode_adamw(const oracle_params *p, const oracle_adamw *w, int64_t n
                         const int32_t *nvalid, int32_t R, const int32_t *slot_idx, const double *slot_val,
                         const double *v, double *theta, double *Q_out)
 {
+    if (p->sign)
+        return -1;
     return decode_impl(p, w, v, n, chunk_id, nvalid, R, slot_idx, slot_val, theta, Q_out);
 }
 

@@ -82,6 +82,37 @@ def test_select_mask_single_draw_is_top_five_bits_of_first_word(torch_philox):
         assert oracle.select_mask(sd, st, ch, 1) == 1 << (int(w[0]) >> 27)
 
 
+def _mask_from_words(blocks, n):
+    """The draw procedure restated: draw i takes word i % 4 of counter block
+    i // 4, scales it to the 32 - i free positions by (w * (32 - i)) >> 32 and
+    takes that free position, counting free positions from bit 0 upward."""
+    mask = 0
+    for i in range(n):
+        w = int(blocks[i // 4][i % 4])
+        r = (w * (N - i)) >> 32
+        free = [b for b in range(N) if not (mask >> b) & 1]
+        mask |= 1 << free[r]
+    return mask
+
+
+@pytest.mark.parametrize("n", [5, 8, 13, 16, 32])
+def test_select_mask_known_answers_over_several_counter_blocks(torch_philox, n):
+    """Masks built here from PyTorch's Philox words of counter blocks 0..7,
+    (chunk_lo, chunk_hi, step_lo, (1 << 24) | block) under key (seed_lo,
+    seed_hi): draws 4 and on take later blocks, so a wrong block number (draw
+    index instead of draw index / 4, a missing tag, a swapped counter word)
+    changes the answer."""
+    cases = [(0, 0, 0), (42, 7, 12345), (2**33 + 9, 2**32 + 3, 19990559), (1, 99, 2**40 + 5),
+             (0xFFFFFFFF, 15, 1), (7, 100, 0)]
+    nblk = (n + 3) // 4
+    blocks = [((ch & 0xFFFFFFFF, ch >> 32, st & 0xFFFFFFFF, (1 << 24) | b), (sd & 0xFFFFFFFF, sd >> 32))
+              for sd, st, ch in cases for b in range(nblk)]
+    words = torch_philox(blocks)
+    for i, (sd, st, ch) in enumerate(cases):
+        want = _mask_from_words(words[i * nblk:(i + 1) * nblk], n)
+        assert oracle.select_mask(sd, st, ch, n) == want, (sd, st, ch, n)
+
+
 def test_select_mask_has_exactly_n_bits_and_is_deterministic():
     for n in range(1, 33):
         for chunk in (0, 1, 12345, 2**35):
