@@ -5,14 +5,16 @@ A step is one pass of the whole path over the shard: demo_encode (momentum,
 32-element chunks, DCT-II, top-k, ternary sign packing, inverse transform,
 error feedback) followed by demo_decode_apply over R replica payloads
 (aggregate, inverse transform, parameter update).  Inputs are synthetic and
-resident in HBM before the timed region: the OLMo2-1B-shaped half shard
-(639,697,920 fp32 parameters), gradients s_layer * N(0, 1e-3) with per-layer
-scales U(0.5, 2), theta ~ N(0, 0.02), momentum from 0; the second replica's
-payload is the encode of a state drawn from seed 1.
+resident in HBM before the timed region: the default workload is the
+OLMo2-1B-shaped half shard (639,697,920 fp32 parameters), gradients
+s_layer * N(0, 1e-3) with per-layer scales U(0.5, 2), theta ~ N(0, 0.02),
+momentum from 0; the second replica's payload is the encode of a state drawn
+from seed 1.
 
 Prints one JSON line.  Timing: W untimed warm-up steps, then K steps between
 two device synchronisations; per-kernel durations come from HIP events
-recorded on the stream the kernels run on.
+recorded on the stream the kernels run on.  The fp64 CPU oracle is timed
+afterwards on the same input bytes (cpu_baseline).
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ import json
 import os
 import sys
 import time
+from dataclasses import dataclass
 
 import numpy as np
 
@@ -30,37 +33,47 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 METRIC = "params/s and HBM GB/s (% of peak) of DeMo encode+decode, OLMo2-1B half shard"
-
-# name: (shard, scheme, k, value format, replicas R, mode); mode "step" = encode + decode
-# per step, "decode" = decode only (R payloads produced before timing)
-WORKLOADS = {
-    "olmo2-1b-half-shard-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-demo-k2": ("olmo2", "dct", 2, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-random-n8": ("olmo2", "random", 8, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-random-n16": ("olmo2", "random", 16, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-random-n8-f16": ("olmo2", "random", 8, "f16", 2, "step"),
-    "olmo2-1b-half-shard-random-n8-f32": ("olmo2", "random", 8, "f32", 2, "step"),
-    "olmo2-1b-half-shard-random-n16-f16": ("olmo2", "random", 16, "f16", 2, "step"),
-    "olmo2-1b-half-shard-random-n16-f32": ("olmo2", "random", 16, "f32", 2, "step"),
-    "olmo2-1b-half-shard-stride-n8": ("olmo2", "stride", 8, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-stride-n16": ("olmo2", "stride", 16, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-diloco-p16": ("olmo2", "diloco", 32, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-decode-r64-demo-k1": ("olmo2", "dct", 1, "ternary", 64, "decode"),
-    "olmo2-1b-half-shard-decode-r64-random-n8": ("olmo2", "random", 8, "ternary", 64, "decode"),
-    "vit-b-set-demo-k1": ("vit", "dct", 1, "ternary", 2, "step"),
-    "olmo2-1b-full-demo-k1": ("olmo2-full", "dct", 1, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-adamw-demo-k1": ("olmo2", "dct", 1, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-adamw-random-n8": ("olmo2", "random", 8, "ternary", 2, "step"),
-    "olmo2-1b-half-shard-demo-k1-f32-sign-off": ("olmo2", "dct", 1, "f32", 2, "step"),
-    "olmo2-1b-half-shard-demo-k1-f16-sign-off": ("olmo2", "dct", 1, "f16", 2, "step"),
-    "olmo2-1b-half-shard-random-n8-f16-sign-off": ("olmo2", "random", 8, "f16", 2, "step"),
-    "olmo2-1b-half-shard-random-n8-f32-sign-off": ("olmo2", "random", 8, "f32", 2, "step"),
-}
-# Decoupled AdamW workloads: second moment v read and written by the encode, read by the decode
-ADAMW = {"olmo2-1b-half-shard-adamw-demo-k1", "olmo2-1b-half-shard-adamw-random-n8"}
-# sign off: the payload slots carry the selected values themselves (DCT coefficients or u)
-SIGN_OFF = {w for w in WORKLOADS if w.endswith("-sign-off")}
 DILOCO_PERIOD = 16
+
+
+@dataclass(frozen=True)
+class Workload:
+    shard: str           # "olmo2" (half shard), "olmo2-full", "vit", "tensor4096"
+    scheme: str          # "dct", "random", "stride", "diloco"
+    k: int
+    fmt: str             # "ternary", "f16", "f32"
+    R: int
+    mode: str = "step"   # "step": encode + decode per step; "decode": decode only
+    sign: int = 1        # 0: the slots carry the selected values themselves
+    adamw: bool = False  # Decoupled AdamW (second moment read and written by the encode)
+
+
+WORKLOADS = {
+    "olmo2-1b-half-shard-demo-k1": Workload("olmo2", "dct", 1, "ternary", 2),
+    "olmo2-1b-half-shard-demo-k2": Workload("olmo2", "dct", 2, "ternary", 2),
+    "olmo2-1b-half-shard-random-n8": Workload("olmo2", "random", 8, "ternary", 2),
+    "olmo2-1b-half-shard-random-n16": Workload("olmo2", "random", 16, "ternary", 2),
+    "olmo2-1b-half-shard-random-n8-f16": Workload("olmo2", "random", 8, "f16", 2),
+    "olmo2-1b-half-shard-random-n8-f32": Workload("olmo2", "random", 8, "f32", 2),
+    "olmo2-1b-half-shard-random-n16-f16": Workload("olmo2", "random", 16, "f16", 2),
+    "olmo2-1b-half-shard-random-n16-f32": Workload("olmo2", "random", 16, "f32", 2),
+    "olmo2-1b-half-shard-stride-n8": Workload("olmo2", "stride", 8, "ternary", 2),
+    "olmo2-1b-half-shard-stride-n16": Workload("olmo2", "stride", 16, "ternary", 2),
+    "olmo2-1b-half-shard-diloco-p16": Workload("olmo2", "diloco", 32, "ternary", 2),
+    "olmo2-1b-half-shard-decode-r64-demo-k1": Workload("olmo2", "dct", 1, "ternary", 64, "decode"),
+    "olmo2-1b-half-shard-decode-r64-random-n8": Workload("olmo2", "random", 8, "ternary", 64, "decode"),
+    "vit-b-set-demo-k1": Workload("vit", "dct", 1, "ternary", 2),
+    "tensor-4096-demo-k4": Workload("tensor4096", "dct", 4, "ternary", 2),
+    "olmo2-1b-full-demo-k1": Workload("olmo2-full", "dct", 1, "ternary", 2),
+    "olmo2-1b-half-shard-adamw-demo-k1-f32": Workload("olmo2", "dct", 1, "f32", 2, sign=0, adamw=True),
+    "olmo2-1b-half-shard-adamw-random-n8-f32": Workload("olmo2", "random", 8, "f32", 2, sign=0, adamw=True),
+    "olmo2-1b-half-shard-demo-k1-f32-sign-off": Workload("olmo2", "dct", 1, "f32", 2, sign=0),
+    "olmo2-1b-half-shard-demo-k1-f16-sign-off": Workload("olmo2", "dct", 1, "f16", 2, sign=0),
+    "olmo2-1b-half-shard-random-n8-f16-sign-off": Workload("olmo2", "random", 8, "f16", 2, sign=0),
+    "olmo2-1b-half-shard-random-n8-f32-sign-off": Workload("olmo2", "random", 8, "f32", 2, sign=0),
+}
+# the 4096-element tensor is L2-resident and launch-bound: no roofline point
+LAUNCH_BOUND = {"tensor-4096-demo-k4"}
 
 
 def _elf_section(path: str, wanted: str) -> bytes:
@@ -92,6 +105,41 @@ def library_hash() -> str:
     return hashlib.sha256(_elf_section(binding.LIB_PATH, ".hip_fatbin")).hexdigest()[:16]
 
 
+class Inputs:
+    """The workload's seeded inputs, drawn on the device (the 4096-element
+    tensor on the host: g, m ~ N(0, 1), theta ~ N(0, 0.02))."""
+
+    def __init__(self, w: Workload, torch, synth):
+        self.w = w
+        self.torch = torch
+        self.synth = synth
+        if w.shard == "tensor4096":
+            self.segs = None
+            self.n = 4096
+        else:
+            self.segs = {"vit": synth.vit_b_set, "olmo2": synth.olmo2_half_shard,
+                         "olmo2-full": synth.olmo2_full}[w.shard]()
+            self.n = synth.shard_numel(self.segs)
+            self.scales = synth.layer_scales(0, max(s.group for s in self.segs) + 1)
+            self.g_std = 1e-2 if w.shard == "vit" else 1e-3
+
+    def grad(self, seed, out=None):
+        if self.segs is None:
+            t = self.torch.from_numpy(self.synth.normal_np(self.n, 1.0, seed, self.synth.TAG_GRAD, 0)).cuda()
+            return t if out is None else out.copy_(t)
+        return self.synth.scaled_grad_torch(self.segs, self.scales, self.g_std, seed, 0, out=out)
+
+    def momentum(self, seed):
+        if self.segs is None:
+            return self.torch.from_numpy(self.synth.normal_np(self.n, 1.0, seed, self.synth.TAG_MOM)).cuda()
+        return self.torch.zeros(self.n, dtype=self.torch.float32, device="cuda")
+
+    def theta(self):
+        if self.segs is None:
+            return self.torch.from_numpy(self.synth.normal_np(self.n, 0.02, 0, self.synth.TAG_THETA)).cuda()
+        return self.synth.normal_torch(self.n, 0.02, 0, self.synth.TAG_THETA)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,17 +167,16 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
-    shard, scheme_name, k, fmt_name, R, mode = WORKLOADS[args.workload]
+    w = WORKLOADS[args.workload]
+    R, mode = w.R, w.mode
     scheme = {"dct": L.SCHEME_DCT, "random": L.SCHEME_RANDOM, "stride": L.SCHEME_STRIDE,
-              "diloco": L.SCHEME_DILOCO}[scheme_name]
-    fmt = {"ternary": L.VAL_TERNARY, "f16": L.VAL_F16, "f32": L.VAL_F32}[fmt_name]
-    segs = {"vit": synth.vit_b_set, "olmo2": synth.olmo2_half_shard, "olmo2-full": synth.olmo2_full}[shard]()
-    n = synth.shard_numel(segs)
-    scales = synth.layer_scales(0, max(s.group for s in segs) + 1)
-    g_std = 1e-2 if shard == "vit" else 1e-3
+              "diloco": L.SCHEME_DILOCO}[w.scheme]
+    fmt = {"ternary": L.VAL_TERNARY, "f16": L.VAL_F16, "f32": L.VAL_F32}[w.fmt]
+    inp = Inputs(w, torch, synth)
+    n = inp.n
 
-    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, beta=0.9, lr=1e-3, seed=0, step=0,
-                   period=DILOCO_PERIOD, sign=0 if args.workload in SIGN_OFF else 1)
+    cfg = L.Config(scheme=scheme, k=w.k, value_fmt=fmt, beta=0.9, lr=1e-3, seed=0, step=0,
+                   period=DILOCO_PERIOD, sign=w.sign)
     lay = L.demo_payload_layout(cfg, n)
     stride = lay["total_bytes"]
     payload_bytes = lay["idx_bytes"] + 2 * lay["plane_bytes"] + lay["val_bytes"]
@@ -137,25 +184,28 @@ def main() -> int:
     def sends(t):
         return scheme != L.SCHEME_DILOCO or t % DILOCO_PERIOD == DILOCO_PERIOD - 1
 
-    adamw = L.AdamW() if args.workload in ADAMW else None
+    adamw = L.AdamW() if w.adamw else None
 
     # ---- inputs, resident in HBM -------------------------------------------
-    g = synth.scaled_grad_torch(segs, scales, g_std, 0, 0)
-    m = torch.zeros(n, dtype=torch.float32, device=dev)
+    g = inp.grad(0)
+    m = inp.momentum(0)
     v = torch.zeros(n, dtype=torch.float32, device=dev) if adamw else None
-    theta = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
+    theta = inp.theta()
     pay = torch.zeros(R * stride, dtype=torch.uint8, device=dev)
-    # the other replicas' payloads: the encode of states drawn from their own
-    # seeds (decode-only workloads: all R replicas, seeds 0..R-1)
+    # the other replicas' payloads: the step-0 encode of states drawn from their
+    # own seeds (decode-only workloads: all R replicas, seeds 0..R-1).  DiLoCo
+    # sends only on sync steps, so its peers encode at the first sync step.
     pg = torch.empty_like(g)
-    pm = torch.empty_like(m)
-    sync_cfg = L.Config(**{**cfg.__dict__, "step": DILOCO_PERIOD - 1})
+    peer_cfg = L.Config(**{**cfg.__dict__, "step": DILOCO_PERIOD - 1 if scheme == L.SCHEME_DILOCO else 0})
     for r in range(1 if mode == "step" else 0, R):
-        synth.scaled_grad_torch(segs, scales, g_std, r, 0, out=pg)
-        pm.zero_()
-        L.demo_encode(sync_cfg, n, pg, pm, pay[r * stride:])
+        inp.grad(r, out=pg)
+        pm = inp.momentum(r)
+        if adamw:
+            L.demo_encode_adamw(peer_cfg, adamw, n, pg, pm, torch.zeros_like(pm), pay[r * stride:])
+        else:
+            L.demo_encode(peer_cfg, n, pg, pm, pay[r * stride:])
     torch.cuda.synchronize()
-    del pg, pm
+    del pg
     torch.cuda.empty_cache()
 
     # ---- achievable copy bandwidth on this device (context) -----------------
@@ -187,12 +237,15 @@ def main() -> int:
         else:
             fn()
 
+    enc_state = (20 if adamw else 12) * n   # g, m (and v) read, m (and v) written
+    dec_state = (12 if adamw else 8) * n    # theta read and written (and v read)
+
     def step(t, record):
         cfg.step = t
         # decode-only workloads decode the step-0 payloads (Random positions of step 0)
         dcfg = cfg if mode == "step" else L.Config(**{**cfg.__dict__, "step": 0})
         if mode == "step":
-            enc_bytes = (20 if adamw else 12) * n + (payload_bytes if sends(t) else 0)
+            enc_bytes = enc_state + (payload_bytes if sends(t) else 0)
             if adamw:
                 timed("encode", enc_bytes, lambda: L.demo_encode_adamw(cfg, adamw, n, g, m, v, pay, None, stream),
                       record)
@@ -200,10 +253,10 @@ def main() -> int:
                 timed("encode", enc_bytes, lambda: L.demo_encode(cfg, n, g, m, pay, None, stream), record)
         if sends(t):
             if adamw:
-                timed("decode", 12 * n + R * payload_bytes,
+                timed("decode", dec_state + R * payload_bytes,
                       lambda: L.demo_decode_apply_adamw(dcfg, adamw, n, theta, v, pay, stride, R, stream), record)
             else:
-                timed("decode", 8 * n + R * payload_bytes,
+                timed("decode", dec_state + R * payload_bytes,
                       lambda: L.demo_decode_apply(dcfg, n, theta, pay, stride, R, stream), record)
 
     for t in range(args.warmup):
@@ -226,7 +279,8 @@ def main() -> int:
         total_bytes += sum(nb)
         kern[kind] = {"calls": len(ms), "avg_ms": float(ms.mean()), "min_ms": float(ms.min()),
                       "bytes": float(np.mean(nb)), "gbps": float(sum(nb) / (ms.sum() / 1e3) / 1e9)}
-    step_gbps = total_bytes / args.steps / (step_ms / 1e3) / 1e9
+    step_bytes = total_bytes / args.steps
+    step_gbps = step_bytes / (step_ms / 1e3) / 1e9
     dom = max(kern, key=lambda kd: kern[kd]["avg_ms"] * kern[kd]["calls"])
     traffic = None
     tfile = os.path.join(ROOT, "profiles", f"traffic_{dom}_{args.workload}.json")
@@ -236,6 +290,11 @@ def main() -> int:
         if rec.get("library_hash") == library_hash():
             traffic = rec.get("hbm_bytes_per_launch")
 
+    if args.workload in LAUNCH_BOUND:
+        roofline = None
+    else:
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["gbps"], "peak": HBM_PEAK_GBPS,
+                    "unit": "GB/s", "frac": kern[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": traffic}
     out = {
         "metric": METRIC,
         "value": n / (step_ms / 1e3),
@@ -249,70 +308,119 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "n_elems": n, "optimizer": "decoupled-adamw" if adamw else "demo-sgd",
-                   "scheme": scheme_name, "k": k, "value_fmt": fmt_name, "sign": cfg.sign,
+        "config": {"workload": args.workload, "n_elems": n,
+                   "optimizer": "decoupled-adamw" if adamw else "demo-sgd",
+                   "scheme": w.scheme, "k": w.k, "value_fmt": w.fmt, "sign": cfg.sign,
                    "replicas": R, "chunk": 32, "mode": mode},
         "hbm_gbps": step_gbps,
         "pct_hbm_peak": 100.0 * step_gbps / HBM_PEAK_GBPS,
         "copy_gbps": copy_gbps,
         "kernels": kern,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["gbps"], "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": kern[dom]["gbps"] / HBM_PEAK_GBPS, "traffic": traffic},
+        "roofline": roofline,
         "cpu_baseline": None,
     }
+    if args.workload in LAUNCH_BOUND:
+        out["launch_bound"] = (f"{n} parameters, {int(step_bytes)} algorithmic bytes per step: L2-resident, "
+                               f"the time is launch and pipeline fill; not a roofline point")
 
-    if not args.no_cpu_baseline and mode == "step" and scheme != L.SCHEME_DILOCO and not adamw:
-        def peer_grad(r):
-            return synth.scaled_grad_torch(segs, scales, g_std, r, 0)
-
-        out["cpu_baseline"] = cpu_baseline(cfg, n, g, m, theta, peer_grad, R, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, cfg, adamw, n, g, m, v, theta, pay, stride, payload_bytes,
+                                           enc_state, dec_state, args.cpu_seconds)
 
     print(json.dumps(out), flush=True)
     return 0
 
 
-def cpu_baseline(cfg, n, g, m, theta, peer_grad, R, budget_s):
-    """The fp64 oracle, timed on this host's cores, on a bounded sample of the
-    same shard: the first S chunks (the same input bytes as the GPU state; the
-    other replicas' slots come from the oracle's own encode of their seeded
-    states), stepped until the CPU budget is used."""
+def cpu_baseline(w, cfg, adamw, n, g, m, v, theta, pay, stride, payload_bytes, enc_state, dec_state, budget_s):
+    """The fp64 oracle as it stands, timed on this host's cores on the same
+    input bytes as the GPU (gradients, state and the other replicas' payloads
+    copied from the device).  A step is what the GPU step does: encode of the
+    own replica and decode of all R payloads (decode-only workloads: the
+    decode; DiLoCo: the average over one period of 16 steps).  The chunks
+    timed are the whole shard when three steps fit the budget on all cores,
+    else its first S chunks; one core runs a smaller sample for a third of the
+    budget.  GB/s uses the GPU's accounting of algorithmic fp32 bytes for the
+    chunks timed (the oracle itself moves fp64 state)."""
     import oracle
 
-    C = n // 32
-    S = min(C, 1 << 21)
-    ids = np.arange(S, dtype=np.uint64)
-    nv = np.full(S, 32, np.int32)
-    zeros = np.zeros((S, 32), np.float32)
-    g_rows = g[: S * 32].view(S, 32).cpu().numpy()
-    own = oracle.Shard(ids, nv, m[: S * 32].view(S, 32).cpu().numpy(), theta[: S * 32].view(S, 32).cpu().numpy())
-    p = oracle.Params(scheme=cfg.scheme, k=cfg.k, sign=cfg.sign, value_fmt=cfg.value_fmt, beta=cfg.beta, lr=cfg.lr,
-                      seed=cfg.seed)
-    peers_idx, peers_val = [], []
-    for r in range(1, R):
-        peer = oracle.Shard(ids, nv, zeros, zeros)
-        gi, gv, _, _ = peer.encode(p, peer_grad(r)[: S * 32].view(S, 32).cpu().numpy())
-        peers_idx.append(gi)
-        peers_val.append(gv)
-    def timed_steps(budget, max_steps):
-        steps = 0
-        t0 = time.perf_counter()
-        while True:
-            idx, val, _, _ = own.encode(p, g_rows)
-            own.decode(p, [idx] + peers_idx, [val] + peers_val)
-            steps += 1
-            if time.perf_counter() - t0 >= budget or steps >= max_steps:
-                return steps, time.perf_counter() - t0
+    from communication_compressed_optimizer_elt_amd import binding as L
+
+    C = (n + 31) // 32
+    p = oracle.Params(scheme=cfg.scheme, k=cfg.k, period=cfg.period, sign=cfg.sign, value_fmt=cfg.value_fmt,
+                      beta=cfg.beta, lr=cfg.lr, seed=cfg.seed, step=0)
+    ow = None if adamw is None else oracle.AdamW(beta2=adamw.beta2, eps=adamw.eps,
+                                                 weight_decay=adamw.weight_decay)
+    decode_only = w.mode == "decode"
+    diloco = cfg.scheme == L.SCHEME_DILOCO
+    period = cfg.period if diloco else 1
+    payload_p = oracle.Params(**{**p.__dict__, "step": cfg.period - 1 if diloco else 0})
+
+    def rows(t, S):
+        return oracle.pad_chunks(t[: min(n, S * 32)].cpu().numpy(), min(n, S * 32))
+
+    def setup(S):
+        """host copies of the first S chunks: own state and the R payloads' slots"""
+        ids = np.arange(S, dtype=np.uint64)
+        nv = np.full(S, 32, np.int32)
+        nv[-1] = min(n, S * 32) - (S - 1) * 32
+        g_rows = rows(g, S)
+        peers = []
+        for r in range(1 if not decode_only else 0, w.R):
+            gi, gv, _ = oracle.unpack(payload_p, n, pay[r * stride:(r + 1) * stride].cpu().numpy(),
+                                      chunks=np.arange(S, dtype=np.uint64))
+            peers.append((gi, gv))
+        own = oracle.Shard(ids, nv, rows(m, S), rows(theta, S), None if v is None else rows(v, S))
+        return own, g_rows, peers
+
+    def run_steps(own, g_rows, peers, nsteps, t0=0):
+        """nsteps oracle steps (DiLoCo: whole periods); returns seconds."""
+        t_start = time.perf_counter()
+        for t in range(t0, t0 + nsteps * period):
+            # decode-only: the step-0 payloads, decoded with step-0 positions as on the GPU
+            pt = oracle.Params(**{**p.__dict__, "step": 0 if decode_only else t})
+            if decode_only:
+                own.decode(pt, [x[0] for x in peers], [x[1] for x in peers], ow)
+                continue
+            idx, val, _, _ = own.encode(pt, g_rows, ow)
+            if oracle.slots(pt):
+                own.decode(pt, [idx] + [x[0] for x in peers], [val] + [x[1] for x in peers], ow)
+        return time.perf_counter() - t_start
+
+    # GPU accounting of one step's algorithmic bytes over the whole shard
+    if decode_only:
+        shard_bytes = dec_state + w.R * payload_bytes
+    else:
+        sync = enc_state + payload_bytes + dec_state + w.R * payload_bytes
+        shard_bytes = (sync + (period - 1) * enc_state) / period
+
+    def measure(budget, steps_wanted):
+        # calibrate on a small sample, then size S to the budget
+        S0 = min(C, 1 << 14)
+        own, g_rows, peers = setup(S0)
+        per_chunk = run_steps(own, g_rows, peers, 1) / S0
+        S = int(min(C, max(S0, budget / max(steps_wanted * per_chunk, 1e-12))))
+        own, g_rows, peers = setup(S)
+        done, dt = 0, 0.0
+        # at least steps_wanted steps and a quarter of the budget (small shards repeat)
+        while (done < steps_wanted or dt < budget / 4) and done < 100000 and not (done and dt >= budget):
+            dt += run_steps(own, g_rows, peers, 1, t0=done * period)
+            done += 1
+        params = min(n, S * 32)
+        steps = done * period
+        what = f"{done} period{'s' if done > 1 else ''} of {period} steps" if period > 1 else \
+            f"{done} step{'s' if done > 1 else ''}"
+        return {"value": params * steps / dt, "unit": "params/s",
+                "gbps": shard_bytes * (params / n) * steps / dt / 1e9,
+                "sample": (f"{'the whole shard' if S == C else f'the first {S} of {C} chunks'} "
+                           f"({params} parameters), {what} in {dt:.2f} s, fp64 state")}
 
     cores = oracle.threads()
-    steps, dt = timed_steps(budget_s, 50)
-    # the same oracle on one core, over a shorter run
+    allc = measure(budget_s, 3)
     oracle.set_threads(1)
-    steps1, dt1 = timed_steps(budget_s / 3, 50)
+    one = measure(budget_s / 3, 1)
     oracle.set_threads(cores)
-    return {"value": S * 32 * steps / dt, "unit": "params/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {S} chunks ({S * 32} params) of the shard, {steps} encode+decode steps "
-                      f"in {dt:.1f} s, fp64 state",
-            "single_core_value": S * 32 * steps1 / dt1,
+    return {"value": allc["value"], "unit": "params/s", "gbps": allc["gbps"], "cores": cores, "kind": "oracle",
+            "sample": allc["sample"], "single_core": {**one, "cores": 1},
             "host": {"cpu": _cpu_model(), "nproc": os.cpu_count()}}
 
 

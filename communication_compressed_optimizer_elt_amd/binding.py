@@ -41,9 +41,9 @@ class demo_cfg(ctypes.Structure):
         ("period", ctypes.c_uint32),
         ("sign", ctypes.c_uint32),
         ("value_fmt", ctypes.c_uint32),
-        ("reserved", ctypes.c_uint32),
         ("beta", ctypes.c_float),
         ("lr", ctypes.c_float),
+        ("reserved", ctypes.c_uint32),
         ("seed", ctypes.c_uint64),
         ("step", ctypes.c_uint64),
         ("chunk_offset", ctypes.c_uint64),
@@ -96,7 +96,7 @@ class Config:
 
     def c(self) -> demo_cfg:
         return demo_cfg(self.abi_version, self.scheme, self.chunk, self.k, self.period, self.sign,
-                        self.value_fmt, self.reserved, self.beta, self.lr, self.seed, self.step,
+                        self.value_fmt, self.beta, self.lr, self.reserved, self.seed, self.step,
                         self.chunk_offset)
 
 

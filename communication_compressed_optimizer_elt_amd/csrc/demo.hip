@@ -196,22 +196,28 @@ hipError_t launch_encode(const demo_cfg* cfg, const EncArgs& a, bool sends, bool
     const unsigned grid = grid_for_groups(a.G);
     if (cfg->scheme == DEMO_SCHEME_DCT) {
         switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: return launch_encode_dct<demo::VF_TERNARY, AD>(a, wq, grid, s);
+        case DEMO_VAL_TERNARY:
+            if constexpr (!AD) return launch_encode_dct<demo::VF_TERNARY, false>(a, wq, grid, s);
+            return hipErrorInvalidValue;  // AdamW carries values (check_adamw)
         case DEMO_VAL_F16: return launch_encode_dct<demo::VF_F16, AD>(a, wq, grid, s);
         default: return launch_encode_dct<demo::VF_F32, AD>(a, wq, grid, s);
         }
     }
     switch (cfg->value_fmt) {
-    case DEMO_VAL_TERNARY: return launch_encode_sel<demo::VF_TERNARY, AD>(a, wq, grid, s);
+    case DEMO_VAL_TERNARY:
+        if constexpr (!AD) return launch_encode_sel<demo::VF_TERNARY, false>(a, wq, grid, s);
+        return hipErrorInvalidValue;
     case DEMO_VAL_F16: return launch_encode_sel<demo::VF_F16, AD>(a, wq, grid, s);
     default: return launch_encode_sel<demo::VF_F32, AD>(a, wq, grid, s);
     }
 }
 
-// AdamW's bias correction 1/(1 - beta1^t) needs beta1 = cfg->beta in [0, 1)
+// AdamW's bias correction 1/(1 - beta1^t) needs beta1 = cfg->beta in [0, 1);
+// its slots carry values (a ternary Q has no magnitude for sqrt(v) to scale)
 int check_adamw(const demo_cfg* cfg, const demo_adamw* w) {
     if (!w) return DEMO_EINVAL;
     if (w->reserved != 0) return DEMO_EINVAL;
+    if (cfg->sign != 0) return DEMO_EINVAL;
     if (!(cfg->beta >= 0.f && cfg->beta < 1.f)) return DEMO_EINVAL;
     if (!(w->beta2 >= 0.f && w->beta2 < 1.f)) return DEMO_EINVAL;
     if (!(w->eps >= 0.f) || !std::isfinite(w->eps) || !std::isfinite(w->weight_decay)) return DEMO_EINVAL;
@@ -310,28 +316,31 @@ template <bool AD>
 hipError_t launch_decode(const demo_cfg* cfg, const DecArgs& a, dim3 grid, dim3 block, hipStream_t s) {
     const uint64_t entries = (uint64_t)a.R * (uint64_t)a.k;  // payload entries per chunk
     const size_t lds = decode_lds_reserve<AD>();  // DCT decodes; the selection decode takes none
-    if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: return launch(demo::decode_dct_kernel<demo::VF_TERNARY, AD>, grid, block, lds, s, a);
-        case DEMO_VAL_F16: return launch(demo::decode_dct_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
-        default: return launch(demo::decode_dct_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
+    if (cfg->value_fmt == DEMO_VAL_TERNARY) {
+        if constexpr (AD) return hipErrorInvalidValue;  // AdamW carries values (check_adamw)
+        else {
+            if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries)
+                return launch(demo::decode_dct_kernel<demo::VF_TERNARY, false>, grid, block, lds, s, a);
+            if (cfg->scheme == DEMO_SCHEME_DCT)
+                return launch(demo::decode_dct_dense_kernel<demo::VF_TERNARY, false>, grid, block, lds, s, a);
+            if (entries > kSelScalarEntries)
+                return launch(demo::decode_sel_kernel<demo::VF_TERNARY, true, false>, grid, block, 0, s, a);
+            return launch(demo::decode_sel_kernel<demo::VF_TERNARY, false, false>, grid, block, 0, s, a);
         }
+    }
+    if (cfg->scheme == DEMO_SCHEME_DCT && entries <= (uint64_t)demo::kSparseEntries) {
+        if (cfg->value_fmt == DEMO_VAL_F16)
+            return launch(demo::decode_dct_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
+        return launch(demo::decode_dct_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
     }
     if (cfg->scheme == DEMO_SCHEME_DCT) {
-        switch (cfg->value_fmt) {
-        case DEMO_VAL_TERNARY: return launch(demo::decode_dct_dense_kernel<demo::VF_TERNARY, AD>, grid, block, lds, s, a);
-        case DEMO_VAL_F16: return launch(demo::decode_dct_dense_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
-        default: return launch(demo::decode_dct_dense_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
-        }
+        if (cfg->value_fmt == DEMO_VAL_F16)
+            return launch(demo::decode_dct_dense_kernel<demo::VF_F16, AD>, grid, block, lds, s, a);
+        return launch(demo::decode_dct_dense_kernel<demo::VF_F32, AD>, grid, block, lds, s, a);
     }
-    switch (cfg->value_fmt) {
-    case DEMO_VAL_TERNARY:
-        if (entries > kSelScalarEntries)
-            return launch(demo::decode_sel_kernel<demo::VF_TERNARY, true, AD>, grid, block, 0, s, a);
-        return launch(demo::decode_sel_kernel<demo::VF_TERNARY, false, AD>, grid, block, 0, s, a);
-    case DEMO_VAL_F16: return launch(demo::decode_sel_kernel<demo::VF_F16, false, AD>, grid, block, 0, s, a);
-    default: return launch(demo::decode_sel_kernel<demo::VF_F32, false, AD>, grid, block, 0, s, a);
-    }
+    if (cfg->value_fmt == DEMO_VAL_F16)
+        return launch(demo::decode_sel_kernel<demo::VF_F16, false, AD>, grid, block, 0, s, a);
+    return launch(demo::decode_sel_kernel<demo::VF_F32, false, AD>, grid, block, 0, s, a);
 }
 
 // demo_decode_apply, and with w (second moment v) demo_decode_apply_adamw

@@ -84,9 +84,9 @@ typedef struct demo_cfg {
                               subnormals kept; needs value_fmt F16 or F32
                               (TERNARY with sign 0 is DEMO_EINVAL). */
     uint32_t value_fmt;    /* DEMO_VAL_* */
-    uint32_t reserved;     /* must be 0 */
-    float beta;            /* momentum decay, finite */
-    float lr;              /* learning rate eta, finite */
+    float beta;            /* momentum decay, finite (offset 28) */
+    float lr;              /* learning rate eta, finite (offset 32) */
+    uint32_t reserved;     /* must be 0; keeps seed at its natural offset 40 */
     uint64_t seed;         /* shared selection seed (RANDOM) */
     uint64_t step;         /* optimizer step t, from 0 (hashed mod 2^32) */
     uint64_t chunk_offset; /* global chunk index of this shard's element 0 */
@@ -126,8 +126,12 @@ typedef struct demo_layout {
  * mean Q as AdamW applies its first moment:
  *   theta -= lr * ((Q / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
  *                  + weight_decay * theta),   t = demo_cfg.step + 1.
- * beta1 (demo_cfg.beta) and beta2 in [0, 1); eps >= 0 and weight_decay finite;
- * reserved must be 0.
+ * The slots carry the selected values (demo_cfg.sign 0, value_fmt F16 or
+ * F32): with the sign before sync ("Sign function" section) Q is a mean of
+ * ternary values that has lost the first moment's magnitude, and dividing it
+ * by sqrt(v) would scale the step by 1/|g|, so demo_cfg.sign 1 is DEMO_EINVAL
+ * for both AdamW calls.  beta1 (demo_cfg.beta) and beta2 in [0, 1); eps >= 0
+ * and weight_decay finite; reserved must be 0.
  */
 typedef struct demo_adamw {
     float beta2;

@@ -39,7 +39,8 @@ int main(void)
 {
     EXPECT(demo_abi_version() == DEMO_ABI_VERSION);
     EXPECT(sizeof(demo_cfg) == 64);
-    EXPECT(offsetof(demo_cfg, beta) == 32 && offsetof(demo_cfg, seed) == 40);
+    EXPECT(offsetof(demo_cfg, beta) == 28 && offsetof(demo_cfg, lr) == 32 && offsetof(demo_cfg, seed) == 40 &&
+           offsetof(demo_cfg, step) == 48 && offsetof(demo_cfg, chunk_offset) == 56);
     EXPECT(sizeof(demo_layout) == 64);
     EXPECT(demo_strerror(DEMO_OK) != NULL && demo_strerror(-99) != NULL);
 

@@ -48,7 +48,8 @@ def test_version_and_strerror(lib):
 
 def test_struct_layout_matches_header(lib):
     assert ctypes.sizeof(L.demo_cfg) == 64
-    assert L.demo_cfg.beta.offset == 32 and L.demo_cfg.seed.offset == 40
+    assert (L.demo_cfg.beta.offset, L.demo_cfg.lr.offset, L.demo_cfg.reserved.offset) == (28, 32, 36)
+    assert (L.demo_cfg.seed.offset, L.demo_cfg.step.offset, L.demo_cfg.chunk_offset.offset) == (40, 48, 56)
     assert ctypes.sizeof(L.demo_layout) == 64
 
 
@@ -175,9 +176,14 @@ def test_plain_c_client(lib, tmp_path):
 
 
 def test_adamw_validation(lib):
-    cfg = _cfg(k=2)
+    cfg = _cfg(k=2, sign=0, value_fmt=L.VAL_F32)
     W = L.AdamW()
     g, m, v, pay = A, 2 * A, 3 * A, 4 * A
+    # the slots carry values: the sign before sync is refused, whatever the format
+    for fmt in (L.VAL_TERNARY, L.VAL_F16, L.VAL_F32):
+        on = _cfg(k=2, sign=1, value_fmt=fmt)
+        assert L.raw_encode_adamw(on, W, 1024, g, m, v, pay) == L.EINVAL
+        assert L.raw_decode_apply_adamw(on, W, 1024, A, v, pay, 4096, 2) == L.EINVAL
     assert L.raw_encode_adamw(cfg, None, 1024, g, m, v, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, L.AdamW(beta2=1.0), 1024, g, m, v, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, L.AdamW(beta2=-0.5), 1024, g, m, v, pay) == L.EINVAL
@@ -185,8 +191,9 @@ def test_adamw_validation(lib):
     assert L.raw_encode_adamw(cfg, L.AdamW(weight_decay=float("nan")), 1024, g, m, v, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, L.AdamW(reserved=1), 1024, g, m, v, pay) == L.EINVAL
     for beta1 in (1.0, 1.5, -0.1):  # the bias correction 1/(1 - beta1^t) needs beta1 in [0, 1)
-        assert L.raw_encode_adamw(_cfg(k=2, beta=beta1), W, 1024, g, m, v, pay) == L.EINVAL
-        assert L.raw_decode_apply_adamw(_cfg(k=2, beta=beta1), W, 1024, A, v, pay, 4096, 2) == L.EINVAL
+        bad = _cfg(k=2, sign=0, value_fmt=L.VAL_F32, beta=beta1)
+        assert L.raw_encode_adamw(bad, W, 1024, g, m, v, pay) == L.EINVAL
+        assert L.raw_decode_apply_adamw(bad, W, 1024, A, v, pay, 4096, 2) == L.EINVAL
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, None, pay) == L.EINVAL
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, v + 4, pay) == L.EALIGN
     assert L.raw_encode_adamw(cfg, W, 1024, g, m, g + 1024, pay) == L.EINVAL  # v overlaps grad
@@ -196,7 +203,8 @@ def test_adamw_validation(lib):
     assert L.raw_decode_apply_adamw(cfg, W, 1024, A, None, pay, lay["total_bytes"], 2) == L.EINVAL
     assert L.raw_decode_apply_adamw(cfg, W, 1024, A, v + 8, pay, lay["total_bytes"], 2) == L.EALIGN
     assert L.raw_decode_apply_adamw(cfg, W, 1024, A, A + 2048, pay, lay["total_bytes"], 2) == L.EINVAL
-    assert L.raw_decode_apply_adamw(_cfg(abi_version=2), W, 1024, A, v, pay, lay["total_bytes"], 2) == L.EABI
+    assert L.raw_decode_apply_adamw(_cfg(abi_version=2, sign=0, value_fmt=L.VAL_F32), W, 1024, A, v, pay,
+                                    lay["total_bytes"], 2) == L.EABI
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

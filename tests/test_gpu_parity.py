@@ -186,27 +186,45 @@ def test_sign_off_fp16_subnormal_values(torch_cuda, scheme, k):
     assert np.sum((np.abs(val) < 2.0 ** -14) & (val != 0)) > val.size // 2
 
 
-@pytest.mark.parametrize("scheme,k,fmt,sign,R", [
-    (L.SCHEME_DCT, 4, L.VAL_TERNARY, 1, 2),
-    (L.SCHEME_DCT, 1, L.VAL_TERNARY, 1, 9),     # many-entry decode
-    (L.SCHEME_DCT, 2, L.VAL_F32, 0, 2),         # values themselves
-    (L.SCHEME_RANDOM, 8, L.VAL_TERNARY, 1, 2),
-    (L.SCHEME_RANDOM, 16, L.VAL_F32, 1, 2),
-    (L.SCHEME_RANDOM, 8, L.VAL_TERNARY, 1, 17),  # bit-sliced counts
-    (L.SCHEME_STRIDE, 8, L.VAL_F16, 1, 2),
-    (L.SCHEME_DILOCO, 32, L.VAL_TERNARY, 1, 2),
+@pytest.mark.parametrize("scheme,k,fmt,R", [
+    (L.SCHEME_DCT, 4, L.VAL_F32, 2),
+    (L.SCHEME_DCT, 1, L.VAL_F32, 9),      # many-entry decode
+    (L.SCHEME_DCT, 2, L.VAL_F16, 2),
+    (L.SCHEME_DCT, 12, L.VAL_F32, 2),     # generic-k encode
+    (L.SCHEME_RANDOM, 8, L.VAL_F32, 2),
+    (L.SCHEME_RANDOM, 16, L.VAL_F16, 2),
+    (L.SCHEME_RANDOM, 8, L.VAL_F32, 17),
+    (L.SCHEME_STRIDE, 8, L.VAL_F16, 2),
+    (L.SCHEME_DILOCO, 32, L.VAL_F32, 2),
 ])
-def test_decoupled_adamw(torch_cuda, scheme, k, fmt, sign, R):
+def test_decoupled_adamw(torch_cuda, scheme, k, fmt, R):
     """Decoupled AdamW: local first and second moments, the first moment
-    extracted and fed back, Q applied with AdamW's scaling and decay."""
-    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=sign, period=4, seed=9)
+    extracted and fed back as values (sign off), Q applied with AdamW's
+    scaling and decay."""
+    cfg = L.Config(scheme=scheme, k=k, value_fmt=fmt, sign=0, period=4, seed=9)
     w = L.AdamW(beta2=0.999, eps=1e-8, weight_decay=0.01)
     _run(torch_cuda, cfg, 32 * 64 * 3 + 17, R, 6, adamw=w)
 
 
+def test_decoupled_adamw_refuses_the_sign(torch_cuda):
+    """With the sign before sync Q has no magnitude for sqrt(v) to scale:
+    both AdamW calls return DEMO_EINVAL and launch nothing."""
+    torch = torch_cuda
+    n = 4096
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=1, sign=1)
+    f = torch.zeros(n, device="cuda")
+    pay = torch.zeros(L.demo_payload_layout(cfg, n)["total_bytes"] * 2, dtype=torch.uint8, device="cuda")
+    with pytest.raises(L.DemoError) as e:
+        L.demo_encode_adamw(cfg, L.AdamW(), n, f, f.clone(), f.clone(), pay)
+    assert e.value.code == L.EINVAL
+    with pytest.raises(L.DemoError) as e:
+        L.demo_decode_apply_adamw(cfg, L.AdamW(), n, f, f.clone(), pay, pay.numel() // 2, 2)
+    assert e.value.code == L.EINVAL
+
+
 def test_decoupled_adamw_eps_and_tail(torch_cuda):
     """eps comparable to sqrt(v) and a ragged last chunk."""
-    cfg = L.Config(scheme=L.SCHEME_DCT, k=3)
+    cfg = L.Config(scheme=L.SCHEME_DCT, k=3, sign=0, value_fmt=L.VAL_F32)
     w = L.AdamW(beta2=0.99, eps=1e-3, weight_decay=0.1)
     _run(torch_cuda, cfg, 4099, 2, 4, adamw=w, g_std=1e-3, m_std=1e-3)
 
@@ -294,12 +312,15 @@ def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, t
         run.set_state(m0, th)
         return run, grads
 
-    cfg = L.Config(scheme=scheme, k=k, period=4, seed=5)
-    straight, grads = fresh(cfg)
+    def config():  # Decoupled AdamW carries values: sign off
+        return L.Config(scheme=scheme, k=k, period=4, seed=5,
+                        **({"sign": 0, "value_fmt": L.VAL_F32} if adam else {}))
+
+    straight, grads = fresh(config())
     for t in range(2 * N):
         straight.step(t, grads(t), check=False)
 
-    first, grads = fresh(L.Config(scheme=scheme, k=k, period=4, seed=5))
+    first, grads = fresh(config())
     for t in range(N):
         first.step(t, grads(t), check=False)
     saved = {"theta": first.theta.cpu(), "step": N}
@@ -311,7 +332,7 @@ def test_resume_from_saved_state_is_bit_identical(torch_cuda, scheme, k, adam, t
     del first
 
     loaded = torch.load(tmp_path / "state.pt", weights_only=True)
-    resumed, grads = fresh(L.Config(scheme=scheme, k=k, period=4, seed=5))
+    resumed, grads = fresh(config())
     resumed.set_state([loaded[f"m{r}"].cuda() for r in range(R)], loaded["theta"].cuda(),
                       [loaded[f"v{r}"].cuda() for r in range(R)] if adam else None)
     for t in range(loaded["step"], 2 * N):
@@ -480,6 +501,8 @@ def _random_configs(count, seed):
         n = int(rng.integers(1, 32 * 64 * 4))
         offset = int(rng.integers(0, 2**40))
         period = int(rng.integers(1, 5))
+        if adam:  # Decoupled AdamW carries values: sign off, fp16 / fp32 slots
+            sign, fmt = 0, (fmt if fmt != L.VAL_TERNARY else L.VAL_F32)
         out.append((i, scheme, k, fmt, sign, R, adam, n, offset, period))
     return out
 
@@ -736,7 +759,7 @@ def test_config3_olmo2_half_shard_every_chunk_first_step(torch_cuda, scheme, k, 
         run.step(t, grads(t))
         print(f"step {t}:", run.report.summary(), f"{time.time() - t0:.1f} s", flush=True)
     assert run.report.ok(), run.report.summary()
-    assert run.report.payload_bytes_compared > 0 or run.report.near_ties + run.report.sign_exceptions > 0
+    assert run.report.payload_bytes_compared > 0
     del run
     torch_cuda.cuda.empty_cache()
 
@@ -770,7 +793,9 @@ def test_olmo2_half_shard_sign_off(torch_cuda, scheme, k, fmt):
 
 @pytest.mark.parametrize("scheme,k", [(L.SCHEME_DCT, 1), (L.SCHEME_RANDOM, 8)])
 def test_config3_olmo2_half_shard_decoupled_adamw(torch_cuda, scheme, k):
-    cfg = L.Config(scheme=scheme, k=k)
+    """Decoupled AdamW on the OLMo2-1B half shard, fp32 value payloads, R = 2,
+    20 steps, sampled chunks."""
+    cfg = L.Config(scheme=scheme, k=k, sign=0, value_fmt=L.VAL_F32)
     segs = synth.olmo2_half_shard()
     _run_full(torch_cuda, cfg, segs, 2, 20, 1999, 4096, 1e-3, scales=synth.layer_scales(0, 18),
               adamw=L.AdamW())
@@ -821,7 +846,8 @@ def test_momentum_only_steps_beyond_2_pow_33_elements(torch_cuda, adamw):
     mark = 2**33 // 32
     sample = np.unique(np.r_[0:2048, C - 2048:C, mark - 1024:mark + 1024, 0:C:999983])
     sample = sample[sample < C]
-    cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16)
+    cfg = L.Config(scheme=L.SCHEME_DILOCO, period=16,
+                   **({"sign": 0, "value_fmt": L.VAL_F32} if adamw is not None else {}))
     run = ParityRun(cfg, n, 1, sample=sample, with_q=False, adamw=adamw)
     m0 = synth.normal_torch(n, 1.0, 0, synth.TAG_MOM)
     th = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
@@ -855,7 +881,9 @@ def test_config4_olmo2_half_shard_diloco(torch_cuda):
 def test_config5_decode_64_replicas(torch_cuda, scheme, k):
     """Receiver side at R = 64: replica r's payload is the step-0 encode of a
     state drawn from seed r; the shard then decodes the 64 payloads in each of
-    50 steps, compared with the oracle after every step."""
+    50 steps, compared with the oracle after every step.  Each payload goes
+    through the oracle's guided encode (near-ties take the GPU's valid top-k,
+    everything else bit-exact), so theta is compared on every sampled chunk."""
     torch = torch_cuda
     segs = synth.olmo2_half_shard()
     n = synth.shard_numel(segs)
@@ -870,12 +898,13 @@ def test_config5_decode_64_replicas(torch_cuda, scheme, k):
     m = torch.empty(n, dtype=torch.float32, device="cuda")
     g = torch.empty(n, dtype=torch.float32, device="cuda")
     th = synth.normal_torch(n, 0.02, 0, synth.TAG_THETA)
-    from harness import _chunk_rows, oracle_params
+    from harness import Report, _chunk_rows, guided_encode
 
     p = oracle_params(cfg)
     nvalid = np.full(len(sample), 32, np.int32)
     ids = sample.astype(np.uint64)
     shard = oracle.Shard(ids, nvalid, np.zeros((len(sample), 32), np.float32), _chunk_rows(th, n, sample))
+    rep = Report()
     idx_l, val_l = [], []
     for r in range(R):
         m.zero_()
@@ -883,16 +912,15 @@ def test_config5_decode_64_replicas(torch_cuda, scheme, k):
         L.demo_encode(cfg, n, g, m, pay[r * stride:])
         torch.cuda.synchronize()
         peer = oracle.Shard(ids, nvalid, np.zeros((len(sample), 32), np.float32), np.zeros((len(sample), 32), np.float32))
-        i_o, v_o, _, _ = peer.encode(p, _chunk_rows(g, n, sample))
         gi, gv, ok = oracle.unpack(p, n, pay[r * stride:(r + 1) * stride].cpu().numpy(), chunks=sample)
-        assert ok
-        same = np.all(gv == v_o, axis=1)
-        if scheme == L.SCHEME_DCT:
-            same &= np.all(gi == i_o, axis=1)
-        assert np.mean(same) > 0.9999, r
-        keep = same if r == 0 else keep & same
+        assert ok, r
+        i_o, v_o, _, _ = guided_encode(rep, f"replica {r}", peer, p, _chunk_rows(g, n, sample), gi, gv, ids)
+        assert np.array_equal(gv, v_o) and (scheme != L.SCHEME_DCT or np.array_equal(gi, i_o)), r
         idx_l.append(i_o)
         val_l.append(v_o)
+    assert not rep.failures, rep.failures[:3]
+    assert rep.near_ties + rep.sign_exceptions <= 3 + 2e-6 * R * len(sample), rep.summary()
+    worst = 0.0
     for t in range(50):
         cfg.step = 0  # the payloads are step-0 payloads; Random positions use step 0
         L.demo_decode_apply(cfg, n, th, pay, stride, R)
@@ -901,7 +929,10 @@ def test_config5_decode_64_replicas(torch_cuda, scheme, k):
         got = _chunk_rows(th, n, sample).astype(np.float64)
         ref = shard.theta
         err = np.max(np.abs(got - ref), axis=1) / np.max(np.abs(ref), axis=1)
-        assert np.max(err[keep]) <= TOL, (t, float(np.max(err[keep])))
+        worst = max(worst, float(np.max(err)))
+        assert np.max(err) <= TOL, (t, float(np.max(err)))
+    print(f"R=64 {'DeMo' if scheme == L.SCHEME_DCT else 'Random'}: {len(sample)} chunks x 50 steps, "
+          f"near_ties={rep.near_ties} sign_exc={rep.sign_exceptions} err_theta={worst:.3g}", flush=True)
     del pay, m, g, th
     torch.cuda.empty_cache()
 
