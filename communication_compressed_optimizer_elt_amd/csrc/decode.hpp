@@ -297,8 +297,11 @@ __device__ __forceinline__ int staged_ternary(const uint4* ws, int e, int lane) 
 }
 
 // DCT scheme, few entries per chunk (R*k <= kSparseEntries): Q accumulated
-// directly from basis rows of an LDS table.
-constexpr int kSparseEntries = 8;
+// directly from basis rows of an LDS table.  Measured on the OLMo2-1B half
+// shard (DeMo, ternary) against the many-entry decode: 2 entries 0.855 against
+// 0.864 ms; 4 entries 0.889 against 0.876 ms (R = 4, k = 1) and 1.017 against
+// 0.905 ms (R = 4, k = 2); 8 entries 1.060 against 0.908 ms.
+constexpr int kSparseEntries = 3;
 
 template <int VF, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
@@ -352,19 +355,31 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
 }
 
 // DCT scheme, many entries per chunk: the entries are summed per frequency in
-// the lane's row of the LDS tile, Q is one full inverse transform of that row.
-// A row belongs to one lane, so the sums are plain LDS read-add-writes in
-// program order (LDS float atomics measured 4x slower here).
+// the lane's own counters in the LDS tile, Q is one full inverse transform of
+// them.  The counters belong to one lane, so the sums are plain LDS
+// read-add-writes (LDS float atomics measured 4x slower here).
 //
-// Ternary payloads (R < 2^15): passes of up to 64 entries stage both the plane
-// words and the index bytes of the pass through LDS with coalesced vector
-// loads; each lane then reads its index byte and its two plane bits per entry
-// from LDS and adds NZ - 2 NEG into an int16 row (exact for R < 2^15).  The
-// tile's 8 KB hold the int16 rows (4 KB) and the staged index bytes (4 KB).
+// Ternary payloads: passes of up to 64 entries stage both the plane words and
+// the index bytes of the pass through LDS with coalesced vector loads; each
+// lane then reads its index byte and its two plane bits per entry from LDS and
+// adds NZ - 2 NEG to its counter of that frequency.  The tile's 8 KB hold the
+// counters (4 KB) and the staged index bytes (4 KB).
+//  - R < 128 (count_entries8): two banks of int8 counters, entries alternating
+//    between them; counter j of a lane sits in a dword of its own column
+//    ((j & 7) * 64 + lane), so a wave's accesses hit 64 distinct banks for any
+//    positions; four entries share one LDS round trip (two per bank, a repeated
+//    position folded into the later write).  The wave runs at raised priority
+//    while its theta and payload loads go out.  Measured on the OLMo2-1B half
+//    shard at R = 64 against int16 rows with one round trip per entry: 1.198
+//    against 1.248 ms, bit-identical (1.211 ms with the priority alone; the
+//    conflict-free layout alone 1.236 ms; more waves per CU without the theta
+//    prefetch, or block-wide staging of the payload, were slower).
+//  - larger R (< 2^15): int16 rows, one read-add-write per entry.
 // Value payloads (and ternary with more replicas): fp32 rows, entries in
 // batches of 16 whose index and value loads go out before the batch's adds.
 constexpr int kDenseBatch = 16;
 constexpr int kRowBytes = kWave * kChunk * 2;  // int16 rows of one wave
+constexpr int kCount8MaxR = 127;               // |counter| <= R fits int8
 
 // index bytes of replicas [r0, r0 + nrep) of group grp (nrep*k <= 64) into
 // is[rl*64k + c*k + s], by 16-byte units; units past the region's entries
@@ -392,6 +407,87 @@ __device__ __forceinline__ void stage_index(const DecArgs& a, uint64_t grp, uint
         if (ok[i]) *reinterpret_cast<uint4*>(is + (lane + i * kWave) * 16) = v[i];
 }
 
+// Ternary entries of all R replicas into two banks of int8 counters (bank A
+// at the tile's bytes [0, 2 KB), bank B at [2 KB, 4 KB); counter j of this
+// lane at byte 4 * ((j & 7) * 64 + lane) + (j >> 3) of its bank), staged index
+// bytes at [4 KB, 8 KB).  Entries 4i, 4i+2 go to bank A, 4i+1, 4i+3 to bank
+// B; the four reads are issued together and, where a bank's two positions
+// coincide, the later write carries both values.  A_j = bank A + bank B.
+// Drops the wave's priority once a pass's loads have landed.
+__device__ __forceinline__ void count_entries8(const DecArgs& a, uint64_t grp, float* st, uint4* ws, int lane,
+                                               float (&A)[32]) {
+    const int k = a.k, R = a.R;
+    uint32_t* cw = reinterpret_cast<uint32_t*>(st);
+    int8_t* cA = reinterpret_cast<int8_t*>(st) + 4 * lane;
+    int8_t* cB = cA + 2048;
+    uint8_t* is = reinterpret_cast<uint8_t*>(st) + kRowBytes;
+#pragma unroll
+    for (int q = 0; q < 16; q++) cw[q * kWave + lane] = 0u;
+    const WordStage w = word_stage(k, lane);
+    const int pass = w.rpr;  // replicas per pass: rpr*k <= 64 entries
+    const uint2* ws2 = reinterpret_cast<const uint2*>(ws) + (lane >> 5);
+    const uint32_t sh = (uint32_t)lane & 31u;
+    const int rowstep = kWave * k - k;  // index-byte offset step when the slot wraps
+    auto at = [](int8_t* bank, int j) { return bank + (j & 7) * (4 * kWave) + (j >> 3); };
+    for (int r0 = 0; r0 < R; r0 += pass) {
+        const int nrep = R - r0 < pass ? R - r0 : pass;
+        const int ne = nrep * k;
+        wave_lds_sync();
+        stage_words<1>(a, grp, ws, w, r0, nrep);
+        stage_index(a, grp, is, r0, nrep, lane);
+        __builtin_amdgcn_s_setprio(0);
+        wave_lds_sync();
+        const uint8_t* il = is + lane * k;  // entry (rl, s) at il[rl*64k + s]
+        int off = 0, s = 0;
+        const int nfull = ne - ne % kDenseBatch;
+        for (int e0 = 0; e0 < nfull; e0 += kDenseBatch) {
+            int jj[kDenseBatch], vi[kDenseBatch];
+#pragma unroll
+            for (int t = 0; t < kDenseBatch; t++) {
+                jj[t] = il[off] & 31;
+                const uint2 h = ws2[2 * (e0 + t)];
+                vi[t] = (int)__builtin_amdgcn_ubfe(h.x, sh, 1u) - 2 * (int)__builtin_amdgcn_ubfe(h.y, sh, 1u);
+                off++;
+                if (++s == k) {
+                    s = 0;
+                    off += rowstep;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < kDenseBatch; t += 4) {
+                int8_t* pa0 = at(cA, jj[t]);
+                int8_t* pb0 = at(cB, jj[t + 1]);
+                int8_t* pa1 = at(cA, jj[t + 2]);
+                int8_t* pb1 = at(cB, jj[t + 3]);
+                const int8_t xa0 = *pa0, xb0 = *pb0, xa1 = *pa1, xb1 = *pb1;
+                const int ya1 = vi[t + 2] + (jj[t] == jj[t + 2] ? vi[t] : 0);
+                const int yb1 = vi[t + 3] + (jj[t + 1] == jj[t + 3] ? vi[t + 1] : 0);
+                *pa0 = (int8_t)(xa0 + vi[t]);
+                *pb0 = (int8_t)(xb0 + vi[t + 1]);
+                *pa1 = (int8_t)(xa1 + ya1);
+                *pb1 = (int8_t)(xb1 + yb1);
+            }
+        }
+        for (int e = nfull; e < ne; e++) {
+            int8_t* p = at(cA, il[off] & 31);
+            *p = (int8_t)(*p + lane_ternary(ws2[2 * e], sh));
+            off++;
+            if (++s == k) {
+                s = 0;
+                off += rowstep;
+            }
+        }
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const uint32_t va = cw[q * kWave + lane], vb = cw[512 + q * kWave + lane];
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+            A[q + 8 * b] = (float)((int)(int8_t)((va >> (8 * b)) & 0xFFu) + (int)(int8_t)((vb >> (8 * b)) & 0xFFu));
+    }
+}
+
 template <int VF, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float stage_all[kWavesPerBlock * kGroupElems];
@@ -404,6 +500,8 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
 
     const uint64_t grp = (uint64_t)xcd_block<kDecodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
     if (grp >= a.G) return;
+    const bool counts8 = VF == VF_TERNARY && R <= kCount8MaxR;
+    if (counts8) __builtin_amdgcn_s_setprio(3);  // while the loads go out
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
     ThetaTile th;  // theta loads go out first
@@ -415,7 +513,9 @@ __global__ __launch_bounds__(kBlock) void decode_dct_dense_kernel(DecArgs a) {
 
     float A[32], Q[32];
     wave_lds_sync();
-    if (VF == VF_TERNARY && R < (1 << 15)) {
+    if (counts8) {
+        count_entries8(a, grp, st, ws, lane, A);
+    } else if (VF == VF_TERNARY && R < (1 << 15)) {
         int16_t* row = reinterpret_cast<int16_t*>(st) + lane * kChunk;
         uint8_t* is = reinterpret_cast<uint8_t*>(st) + kRowBytes;
 #pragma unroll

@@ -131,7 +131,7 @@ def test_many_replicas(torch_cuda, scheme, k, fmt, R):
     _run(torch_cuda, cfg, 32 * 64 * 5 + 33, R, 2)
 
 
-@pytest.mark.parametrize("R", [9, 255, 256])
+@pytest.mark.parametrize("R", [9, 64, 127, 128, 255, 256])
 def test_dct_decode_of_identical_payloads(torch_cuda, R):
     """R copies of one DeMo k=1 payload put all R entries of a chunk on one
     frequency, the largest per-frequency sums the many-entry decode forms:
