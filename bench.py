@@ -13,7 +13,7 @@ from seed 1.
 
 Prints one JSON line.  Timing: W untimed warm-up steps, then K steps between
 two device synchronisations; per-kernel durations come from HIP events
-recorded on the stream the kernels run on.  The fp64 CPU oracle is timed
+recorded between the launches on the stream the kernels run on.  The fp64 CPU oracle is timed
 afterwards on the same input bytes (cpu_baseline).
 """
 from __future__ import annotations
@@ -224,18 +224,26 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     stream = torch.cuda.current_stream()
-    # per timed call: (kind, start event, end event, algorithmic bytes)
+    # per timed call: (kind, start event, end event, algorithmic bytes).  The
+    # events are chained: one event between consecutive launches marks the end
+    # of one call and the start of the next (a pair of events around every
+    # call measured 10-20 us more per step), so a call's interval also holds
+    # the dispatch gap after the previous kernel.
     calls = []
+    boundary = [None]
 
     def timed(kind, nbytes, fn, record):
-        if record:
-            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ea.record(stream)
+        if not record:
             fn()
-            eb.record(stream)
-            calls.append((kind, ea, eb, nbytes))
-        else:
-            fn()
+            return
+        if boundary[0] is None:
+            boundary[0] = torch.cuda.Event(enable_timing=True)
+            boundary[0].record(stream)
+        fn()
+        eb = torch.cuda.Event(enable_timing=True)
+        eb.record(stream)
+        calls.append((kind, boundary[0], eb, nbytes))
+        boundary[0] = eb
 
     enc_state = (20 if adamw else 12) * n   # g, m (and v) read, m (and v) written
     dec_state = (12 if adamw else 8) * n    # theta read and written (and v read)
