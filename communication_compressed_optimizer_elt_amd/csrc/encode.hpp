@@ -43,9 +43,10 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
         float X[32];
         dct32(u, X);
 
-        float q[32];
+        float q[32], mo[32];  // extracted component and feedback m' = u - q
 #pragma unroll
         for (int i = 0; i < 32; i++) q[i] = 0.f;
+        bool mo_done = false;  // the generic-k form may produce m' directly
 
         uint64_t mynz = 0, myneg = 0;
 
@@ -165,10 +166,22 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
 #pragma unroll
                 for (int j = 0; j < 32; j++) ax[j] = (j == bj) ? -1.f : ax[j];
             }
+            // With more than half the coefficients kept, m' is taken as the
+            // inverse transform of the ones left behind and q = u - m' (the same
+            // values: its rounding then scales with the smaller, unselected
+            // coefficients, and k = 32 gives m' = 0 and q = u exactly).
+            const bool rest = 2 * k > kChunk;
             float Xs[32];
 #pragma unroll
-            for (int j = 0; j < 32; j++) Xs[j] = ((S >> j) & 1u) ? X[j] : 0.f;
-            idct32(Xs, q);
+            for (int j = 0; j < 32; j++) Xs[j] = (((S >> j) & 1u) != 0u) != rest ? X[j] : 0.f;
+            if (rest) {
+                idct32(Xs, mo);
+#pragma unroll
+                for (int i = 0; i < 32; i++) q[i] = u[i] - mo[i];
+                mo_done = true;
+            } else {
+                idct32(Xs, q);
+            }
             // slots in ascending position order
             uint32_t nzv = 0, negv = 0;
             int s = 0;
@@ -206,9 +219,10 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
         }
 
         // m <- u - q, back through LDS to coalesced order
-        float mo[32];
+        if (!mo_done) {
 #pragma unroll
-        for (int i = 0; i < 32; i++) mo[i] = u[i] - q[i];
+            for (int i = 0; i < 32; i++) mo[i] = u[i] - q[i];
+        }
         put_chunk(st, lane, mo);
         wave_lds_sync();
         float4 outc[8];
