@@ -238,7 +238,7 @@ __device__ __forceinline__ void apply_update_prefetched(const DecArgs& a, const 
         tv.y = fmaf(-a.lr, qc[r].y, tv.y);
         tv.z = fmaf(-a.lr, qc[r].z, tv.z);
         tv.w = fmaf(-a.lr, qc[r].w, tv.w);
-        t4[r * kWave + lane] = tv;
+        store_stream(t4 + r * kWave + lane, tv);
     }
 }
 

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
         const bool valid = c < a.C;
 
         float4 uc[8];
-        load_u<AD>(a, base, full, lane, uc);
+        load_u<AD, !AD>(a, base, full, lane, uc);
         wave_lds_sync();
         put_coalesced(st, lane, uc);
         wave_lds_sync();
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kBlock) void encode_dct_kernel(EncArgs a) {
         wave_lds_sync();
         float4 outc[8];
         get_coalesced(st, lane, outc);
-        store_tile(a.m, base, a.n, full, lane, outc);
+        store_tile<!AD>(a.m, base, a.n, full, lane, outc);
         if constexpr (WQ) {
             wave_lds_sync();
             put_chunk(st, lane, q);
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
         const bool valid = c < a.C;
 
         float4 uc[8];
-        load_u<AD>(a, base, full, lane, uc);
+        load_u<AD, !AD>(a, base, full, lane, uc);
         wave_lds_sync();
         put_coalesced(st, lane, uc);
         wave_lds_sync();
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
         wave_lds_sync();
         float4 outc[8];
         get_coalesced(st, lane, outc);
-        store_tile(a.m, base, a.n, full, lane, outc);
+        store_tile<!AD>(a.m, base, a.n, full, lane, outc);
         if constexpr (WQ) {
             float q[32];
 #pragma unroll
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
     for (uint64_t i = i0; i < n4; i += step) {
         const float4 gv = load_stream(reinterpret_cast<const float4*>(a.g) + i);
         float4* m4 = reinterpret_cast<float4*>(a.m);
-        float4 mv = m4[i];
+        float4 mv = AD ? m4[i] : load_stream(m4 + i);
         if constexpr (AD) {
             float4* v4 = reinterpret_cast<float4*>(a.v);
             float4 vv = v4[i];
@@ -397,7 +397,10 @@ __global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
         mv.y = fmaf(a.beta, mv.y, AD ? a.gamma * gv.y : gv.y);
         mv.z = fmaf(a.beta, mv.z, AD ? a.gamma * gv.z : gv.z);
         mv.w = fmaf(a.beta, mv.w, AD ? a.gamma * gv.w : gv.w);
-        m4[i] = mv;
+        if constexpr (AD)
+            m4[i] = mv;
+        else
+            store_stream(m4 + i, mv);
         if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (i0 < (a.n & 3)) {

@@ -61,14 +61,34 @@ __device__ __forceinline__ float4 load_stream(const float4* p) {
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
+// write-once stream: non-temporal store (the line is not read again in the
+// launch, and the next step reaches it only after gigabytes of other traffic).
+// Measured on the OLMo2-1B half shard, one box, interleaved minima: the
+// momentum read and rewritten by non-temporal loads and stores, DeMo k = 1
+// encode 1.248 -> 1.160 ms, Random n = 8 encode 1.269 -> 1.168 ms, DiLoCo
+// momentum pass 1.315 -> 1.241 ms (non-temporal loads alone 1.228 -> 1.278
+// ms, stores alone 1.269 -> 1.323 ms on the Random encode: only the pair
+// pays); theta stored so in the decodes, DeMo k = 1 0.847 -> 0.803 ms, R = 64
+// 1.207 -> 1.139 ms, Random n = 8 0.858 -> 0.822 ms.  Decoupled AdamW: its
+// second moment stored so, DCT encode 2.198 -> 2.130 ms, but the momentum
+// there stays on plain loads and stores (2.240 ms with both non-temporal),
+// and theta in its decodes too (Random n = 8 decode 1.525 -> 1.590 ms with
+// non-temporal stores).
+__device__ __forceinline__ void store_stream(float4* p, float4 v) {
+    __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+
 // AdamW second moment: beta2*v + (1 - beta2)*g^2
 __device__ __forceinline__ float second_moment(const EncArgs& a, float v, float g) {
     return fmaf(a.beta2, v, (1.f - a.beta2) * (g * g));
 }
 
 // u = beta*m + gamma*g for the wave's group, coalesced order; zero beyond n
-// (with AdamW the second moment is updated in the same pass).
-template <bool AD>
+// (with AdamW the second moment is updated in the same pass, its new value
+// written by non-temporal stores).  NTM: m is read by non-temporal loads (its
+// lines are rewritten by the same wave; pays only together with non-temporal
+// stores of m).
+template <bool AD, bool NTM>
 __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool full, int lane, float4 (&uc)[8]) {
     if (full) {
         const float4* g4 = reinterpret_cast<const float4*>(a.g + base);
@@ -77,7 +97,7 @@ __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool ful
 #pragma unroll
         for (int r = 0; r < 8; r++) {
             gv[r] = load_stream(g4 + r * kWave + lane);
-            mv[r] = m4[r * kWave + lane];
+            mv[r] = NTM ? load_stream(m4 + r * kWave + lane) : m4[r * kWave + lane];
         }
         if constexpr (AD) {
             float4* v4 = reinterpret_cast<float4*>(a.v + base);
@@ -88,7 +108,7 @@ __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool ful
                 vv.y = second_moment(a, vv.y, gv[r].y);
                 vv.z = second_moment(a, vv.z, gv[r].z);
                 vv.w = second_moment(a, vv.w, gv[r].w);
-                v4[r * kWave + lane] = vv;
+                store_stream(v4 + r * kWave + lane, vv);
             }
         }
 #pragma unroll
@@ -147,13 +167,20 @@ __device__ __forceinline__ void get_chunk(const float* st, int lane, float (&x)[
     }
 }
 
-// store a coalesced tile to dst[base ...], guarded beyond n
+// store a coalesced tile to dst[base ...], guarded beyond n (NT: whole tiles
+// by non-temporal stores)
+template <bool NT = false>
 __device__ __forceinline__ void store_tile(float* dst, uint64_t base, uint64_t n, bool full, int lane,
                                            const float4 (&v)[8]) {
     if (full) {
         float4* d4 = reinterpret_cast<float4*>(dst + base);
 #pragma unroll
-        for (int r = 0; r < 8; r++) d4[r * kWave + lane] = v[r];
+        for (int r = 0; r < 8; r++) {
+            if constexpr (NT)
+                store_stream(d4 + r * kWave + lane, v[r]);
+            else
+                d4[r * kWave + lane] = v[r];
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < 8; r++) {
