@@ -383,14 +383,22 @@ constexpr int kCount8MaxR = 127;               // |counter| <= R fits int8
 
 // index bytes of replicas [r0, r0 + nrep) of group grp (nrep*k <= 64) into
 // is[rl*64k + c*k + s], by 16-byte units; units past the region's entries
-// (the last group) are skipped
+// (the last group) are skipped.  From 16 entries per chunk (R*k) on, the
+// loads are non-temporal.  Measured on the OLMo2-1B half shard, DeMo decode,
+// one box: k = 1, R = 16 879 -> 866 us, R = 48 1030 -> 1010 us; k = 2, R = 8
+// 885 -> 868 us, R = 32 1110 -> 1059 us, R = 64 1917 -> 1558 us; with fewer
+// entries they were 2-3% slower (k = 1, R = 8 815 -> 841 us).
+constexpr int kStreamIndexEntries = 16;
+
 __device__ __forceinline__ void stage_index(const DecArgs& a, uint64_t grp, uint8_t* is, int r0, int nrep,
                                             int lane) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     const int k = a.k;
     const int upr = 4 * k;  // 16-byte units per replica row of 64k bytes
     const uint64_t g0 = grp * (uint64_t)(kWave * k);
     const uint64_t lim = a.C * (uint64_t)k;
     const int units = nrep * upr;  // <= 256
+    const bool stream = a.R * k >= kStreamIndexEntries;
     uint4 v[4];
     bool ok[4];
 #pragma unroll
@@ -400,7 +408,9 @@ __device__ __forceinline__ void stage_index(const DecArgs& a, uint64_t grp, uint
         ok[i] = u < units && g0 + off < lim;
         const int rc = ok[i] ? r0 + rl : r0;
         const uint64_t oc = ok[i] ? (uint64_t)off : 0;
-        v[i] = *reinterpret_cast<const uint4*>(a.pay + (uint64_t)rc * a.stride + a.idx_off + g0 + oc);
+        const u32x4* p = reinterpret_cast<const u32x4*>(a.pay + (uint64_t)rc * a.stride + a.idx_off + g0 + oc);
+        const u32x4 t = stream ? __builtin_nontemporal_load(p) : *p;
+        v[i] = make_uint4(t.x, t.y, t.z, t.w);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++)

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
         const bool valid = c < a.C;
 
         float4 uc[8];
-        load_u<AD, !AD>(a, base, full, lane, uc);
+        load_u<AD, true>(a, base, full, lane, uc);
         wave_lds_sync();
         put_coalesced(st, lane, uc);
         wave_lds_sync();
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
         wave_lds_sync();
         float4 outc[8];
         get_coalesced(st, lane, outc);
-        store_tile<!AD>(a.m, base, a.n, full, lane, outc);
+        store_tile<true>(a.m, base, a.n, full, lane, outc);
         if constexpr (WQ) {
             float q[32];
 #pragma unroll

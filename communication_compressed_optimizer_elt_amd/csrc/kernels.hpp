@@ -69,11 +69,12 @@ __device__ __forceinline__ float4 load_stream(const float4* p) {
 // momentum pass 1.315 -> 1.241 ms (non-temporal loads alone 1.228 -> 1.278
 // ms, stores alone 1.269 -> 1.323 ms on the Random encode: only the pair
 // pays); theta stored so in the decodes, DeMo k = 1 0.847 -> 0.803 ms, R = 64
-// 1.207 -> 1.139 ms, Random n = 8 0.858 -> 0.822 ms.  Decoupled AdamW: its
-// second moment stored so, DCT encode 2.198 -> 2.130 ms, but the momentum
-// there stays on plain loads and stores (2.240 ms with both non-temporal),
-// and theta in its decodes too (Random n = 8 decode 1.525 -> 1.590 ms with
-// non-temporal stores).
+// 1.207 -> 1.139 ms, Random n = 8 0.858 -> 0.822 ms.  Decoupled AdamW, fp32
+// values: the second moment read and rewritten so, DCT encode 2.198 -> 2.055
+// ms, Random n = 8 encode 2.352 -> 2.295 ms; its momentum too in the Random
+// encode (-> 2.189 ms) but not in the DCT encode (2.300 ms with it); theta in
+// its decodes stays on plain stores (Random n = 8 decode 1.525 -> 1.590 ms
+// with non-temporal ones).
 __device__ __forceinline__ void store_stream(float4* p, float4 v) {
     __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
@@ -84,10 +85,10 @@ __device__ __forceinline__ float second_moment(const EncArgs& a, float v, float 
 }
 
 // u = beta*m + gamma*g for the wave's group, coalesced order; zero beyond n
-// (with AdamW the second moment is updated in the same pass, its new value
-// written by non-temporal stores).  NTM: m is read by non-temporal loads (its
-// lines are rewritten by the same wave; pays only together with non-temporal
-// stores of m).
+// (with AdamW the second moment is updated in the same pass, read and
+// written by non-temporal loads and stores).  NTM: m is read by non-temporal
+// loads (its lines are rewritten by the same wave; pays only together with
+// non-temporal stores of m).
 template <bool AD, bool NTM>
 __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool full, int lane, float4 (&uc)[8]) {
     if (full) {
@@ -103,7 +104,7 @@ __device__ __forceinline__ void load_u(const EncArgs& a, uint64_t base, bool ful
             float4* v4 = reinterpret_cast<float4*>(a.v + base);
 #pragma unroll
             for (int r = 0; r < 8; r++) {
-                float4 vv = v4[r * kWave + lane];
+                float4 vv = load_stream(v4 + r * kWave + lane);
                 vv.x = second_moment(a, vv.x, gv[r].x);
                 vv.y = second_moment(a, vv.y, gv[r].y);
                 vv.z = second_moment(a, vv.z, gv[r].z);
