@@ -46,12 +46,17 @@ __device__ __forceinline__ void wave_lds_sync() {
 // The run length is the kernel's: on the OLMo2-1B half shard (639,697,920
 // parameters) the encodes measured fastest with S = 4 (DeMo k = 1: 1.244 ms
 // against 1.302 ms with one contiguous range per XCD; Random n = 8: 1.273
-// against 1.308 ms) and the decodes with S = 16 (0.905 against 0.925 ms;
-// 1.255 against 1.274 ms at R = 64); run lengths that are not powers of two
-// (2, 3, 6, 12, 24) measured slower.
+// against 1.308 ms; with non-temporal momentum streams 1.160 against 1.184 ms
+// at S = 8 and 1.203 ms at S = 2).  The decodes, whose theta is stored by
+// non-temporal stores, run fastest with S = 8 (DeMo k = 1: 0.786 against
+// 0.804 ms at S = 16 and 0.838 ms at S = 4; Random n = 8: 0.790 against 0.815
+// ms; R = 64 equal or faster), except the Decoupled AdamW few-entry DCT decode
+// (plain theta stores), which keeps S = 16 (1.317 against 1.376 ms at S = 8).
+// Run lengths that are not powers of two (2, 3, 6, 12, 24) measured slower.
 constexpr uint32_t kXcds = 8;
 constexpr uint32_t kEncodeRun = 4;
-constexpr uint32_t kDecodeRun = 16;
+constexpr uint32_t kDecodeRun = 8;
+constexpr uint32_t kDecodeRunAdamwDct = 16;
 
 template <uint32_t S>
 __device__ __forceinline__ uint32_t xcd_block(uint32_t b, uint32_t nb) {
