@@ -298,10 +298,12 @@ __device__ __forceinline__ int staged_ternary(const uint4* ws, int e, int lane) 
 
 // DCT scheme, few entries per chunk (R*k <= kSparseEntries): Q accumulated
 // directly from basis rows of an LDS table.  Measured on the OLMo2-1B half
-// shard (DeMo, ternary) against the many-entry decode: 2 entries 0.855 against
-// 0.864 ms; 4 entries 0.889 against 0.876 ms (R = 4, k = 1) and 1.017 against
-// 0.905 ms (R = 4, k = 2); 8 entries 1.060 against 0.908 ms.
-constexpr int kSparseEntries = 3;
+// shard (DeMo, ternary) against the many-entry decode, both with non-temporal
+// theta stores: 4 entries 0.793 against 0.834 ms (R = 4, k = 1) and 0.794
+// against 0.835 ms (R = 2, k = 2); 6 entries 0.840 against 0.835 ms; 8
+// entries 0.911 against 0.839 ms (R = 8, k = 1) and 0.893 against 0.838 ms
+// (R = 4, k = 2).
+constexpr int kSparseEntries = 4;
 
 template <int VF, bool AD>
 __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {

@@ -372,42 +372,23 @@ __global__ __launch_bounds__(kBlock) void encode_sel_kernel(EncArgs a) {
     }
 }
 
-// DiLoCo between synchronisations: m <- beta*m + g, nothing extracted.  One
-// float4 per work-item and pass over the grid (a single pass unless the grid
-// was capped); work-items 0-2 also take the 0-3 trailing elements.
+// DiLoCo between synchronisations: m <- beta*m + g (with AdamW also v),
+// nothing extracted.  One wave per 2048-element group, through the encodes'
+// load and store paths.
 template <bool WQ, bool AD>
-__global__ __launch_bounds__(256) void momentum_kernel(EncArgs a) {
-    const uint64_t n4 = a.n / 4;
-    const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
-    for (uint64_t i = i0; i < n4; i += step) {
-        const float4 gv = load_stream(reinterpret_cast<const float4*>(a.g) + i);
-        float4* m4 = reinterpret_cast<float4*>(a.m);
-        float4 mv = AD ? m4[i] : load_stream(m4 + i);
-        if constexpr (AD) {
-            float4* v4 = reinterpret_cast<float4*>(a.v);
-            float4 vv = v4[i];
-            vv.x = second_moment(a, vv.x, gv.x);
-            vv.y = second_moment(a, vv.y, gv.y);
-            vv.z = second_moment(a, vv.z, gv.z);
-            vv.w = second_moment(a, vv.w, gv.w);
-            v4[i] = vv;
-        }
-        mv.x = fmaf(a.beta, mv.x, AD ? a.gamma * gv.x : gv.x);
-        mv.y = fmaf(a.beta, mv.y, AD ? a.gamma * gv.y : gv.y);
-        mv.z = fmaf(a.beta, mv.z, AD ? a.gamma * gv.z : gv.z);
-        mv.w = fmaf(a.beta, mv.w, AD ? a.gamma * gv.w : gv.w);
-        if constexpr (AD)
-            m4[i] = mv;
-        else
-            store_stream(m4 + i, mv);
-        if (WQ) reinterpret_cast<float4*>(a.q_out)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (i0 < (a.n & 3)) {
-        const uint64_t e = n4 * 4 + i0;
-        if constexpr (AD) a.v[e] = second_moment(a, a.v[e], a.g[e]);
-        a.m[e] = fmaf(a.beta, a.m[e], AD ? a.gamma * a.g[e] : a.g[e]);
-        if (WQ) a.q_out[e] = 0.f;
+__global__ __launch_bounds__(kBlock) void momentum_kernel(EncArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint64_t grp = (uint64_t)xcd_block<kMomentumRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+    if (grp >= a.G) return;
+    const uint64_t base = grp * kGroupElems;
+    const bool full = base + kGroupElems <= a.n;
+    float4 uc[8];
+    load_u<AD, !AD>(a, base, full, lane, uc);
+    store_tile<!AD>(a.m, base, a.n, full, lane, uc);
+    if constexpr (WQ) {
+        const float4 z[8] = {};
+        store_tile(a.q_out, base, a.n, full, lane, z);
     }
 }
 

@@ -834,10 +834,10 @@ def test_shard_beyond_2_pow_32_elements(torch_cuda):
 
 @pytest.mark.parametrize("adamw", [None, L.AdamW()])
 def test_momentum_only_steps_beyond_2_pow_33_elements(torch_cuda, adamw):
-    """DiLoCo steps between synchronisations stream one float4 per work-item
-    and pass; at n = 2^33 + 1029 the grid is capped and 257 float4 and one
-    trailing element fall to a second pass.  Sampled chunks at both ends and
-    around the 2^33 element mark, steps 0 and 1 of period 16."""
+    """DiLoCo steps between synchronisations at n = 2^33 + 1029: the momentum
+    pass's one-pass group grid past 2^22 groups (element offsets beyond 32
+    bits in every wave), a ragged last group of 1029 elements.  Sampled chunks
+    at both ends and around the 2^33 element mark, steps 0 and 1 of period 16."""
     torch = torch_cuda
     if torch.cuda.get_device_properties(0).total_memory < 200 * 2**30:
         pytest.skip("needs about 130 GB of device memory")
