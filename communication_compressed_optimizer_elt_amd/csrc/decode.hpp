@@ -170,10 +170,14 @@ __device__ __forceinline__ void prefetch_theta(const DecArgs& a, uint64_t base, 
     }
 }
 
-// Decoupled AdamW, few-entry DCT decode: the read-only second moment v is the
-// tile loaded up front (non-temporal, like theta elsewhere) and theta is
-// read after Q.  Measured on the OLMo2-1B half shard: 1.265 ms against 1.336
-// ms with both loaded after Q, and against 1.506 ms with theta prefetched.
+// Decoupled AdamW decodes: the read-only second moment v is the tile loaded up
+// front (non-temporal, like theta elsewhere) and theta is read after Q, by
+// non-temporal loads, and stored the same way.  Measured on the OLMo2-1B half
+// shard, few-entry DCT decode: 1.265 ms against 1.336 ms with both loaded
+// after Q and 1.506 ms with theta prefetched (plain theta accesses); with the
+// non-temporal theta load and store 1.329 -> 1.206 ms (the load alone: 1.440
+// ms).  Selection decode (Random n = 8): 1.507 ms with theta prefetched too
+// and stored plainly, 1.433 ms this way.
 __device__ __forceinline__ void prefetch_moment2(const DecArgs& a, uint64_t base, bool full, int lane, ThetaTile& t) {
     if (full) {
         const float4* v4 = reinterpret_cast<const float4*>(a.v + base);
@@ -192,27 +196,9 @@ __device__ __forceinline__ void apply_adamw_moment2_prefetched(const DecArgs& a,
     get_coalesced(st, lane, qc);
     float4* t4 = reinterpret_cast<float4*>(a.theta + base);
 #pragma unroll
-    for (int r = 0; r < 8; r++) tv[r] = t4[r * kWave + lane];
+    for (int r = 0; r < 8; r++) tv[r] = load_stream(t4 + r * kWave + lane);
 #pragma unroll
-    for (int r = 0; r < 8; r++) t4[r * kWave + lane] = adamw_step4(a, tv[r], qc[r], v.v[r]);
-}
-
-// Decoupled AdamW, selection decode: theta and v both loaded up front
-// (non-temporal).  Measured on the OLMo2-1B half shard, Random n = 8: 1.300
-// ms against 1.363 ms with v read after the slot sums (n = 16: 1.441 against
-// 1.495 ms).
-__device__ __forceinline__ void apply_adamw_both_prefetched(const DecArgs& a, const float* st, uint64_t base,
-                                                            bool full, int lane, const ThetaTile& th,
-                                                            const ThetaTile& v) {
-    if (!full) {
-        apply_update<true>(a, st, base, full, lane);
-        return;
-    }
-    float4 qc[8];
-    get_coalesced(st, lane, qc);
-    float4* t4 = reinterpret_cast<float4*>(a.theta + base);
-#pragma unroll
-    for (int r = 0; r < 8; r++) t4[r * kWave + lane] = adamw_step4(a, th.v[r], qc[r], v.v[r]);
+    for (int r = 0; r < 8; r++) store_stream(t4 + r * kWave + lane, adamw_step4(a, tv[r], qc[r], v.v[r]));
 }
 
 template <bool AD>
@@ -757,9 +743,11 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
-    ThetaTile th, vt;  // theta (and AdamW's read-only v) loads go out first
-    prefetch_theta(a, base, full, lane, th);
-    if constexpr (AD) prefetch_moment2(a, base, full, lane, vt);
+    ThetaTile th;  // theta (AdamW: the read-only v) loads go out first
+    if constexpr (AD)
+        prefetch_moment2(a, base, full, lane, th);
+    else
+        prefetch_theta(a, base, full, lane, th);
     const uint64_t c = grp * kWave + lane;
     const bool valid = c < a.C;
     const uint64_t cv = valid ? c : 0;
@@ -835,7 +823,7 @@ __global__ __launch_bounds__(kBlock) void decode_sel_kernel(DecArgs a) {
         }
     wave_lds_sync();
     if constexpr (AD)
-        apply_adamw_both_prefetched(a, st, base, full, lane, th, vt);
+        apply_adamw_moment2_prefetched(a, st, base, full, lane, th);
     else
         apply_update_prefetched<AD>(a, st, base, full, lane, th);
 }

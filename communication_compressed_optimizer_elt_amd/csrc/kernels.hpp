@@ -72,9 +72,9 @@ __device__ __forceinline__ float4 load_stream(const float4* p) {
 // 1.207 -> 1.139 ms, Random n = 8 0.858 -> 0.822 ms.  Decoupled AdamW, fp32
 // values: the second moment read and rewritten so, DCT encode 2.198 -> 2.055
 // ms, Random n = 8 encode 2.352 -> 2.295 ms; its momentum too in the Random
-// encode (-> 2.189 ms) but not in the DCT encode (2.300 ms with it); theta in
-// its decodes stays on plain stores (Random n = 8 decode 1.525 -> 1.590 ms
-// with non-temporal ones).
+// encode (-> 2.189 ms) but not in the DCT encode (2.300 ms with it); its
+// decodes read theta after Q and rewrite it the same way (DCT 1.329 -> 1.206
+// ms, Random n = 8 1.507 -> 1.433 ms).
 __device__ __forceinline__ void store_stream(float4* p, float4 v) {
     __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
 }
