@@ -301,7 +301,8 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     float* st = stage_all + wv * kGroupElems;
     const int k = a.k, R = a.R;
 
-    const uint64_t grp = (uint64_t)xcd_block<AD ? kDecodeRunAdamwDct : kDecodeRun>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
+    constexpr uint32_t run = AD ? kDecodeRunAdamwDct : kDecodeRun;
+    const uint64_t grp = (uint64_t)xcd_block<run>(blockIdx.x, gridDim.x) * kWavesPerBlock + wv;
     if (grp >= a.G) return;
     const uint64_t base = grp * kGroupElems;
     const bool full = base + kGroupElems <= a.n;
