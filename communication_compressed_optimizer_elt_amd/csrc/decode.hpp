@@ -311,9 +311,9 @@ __global__ __launch_bounds__(kBlock) void decode_dct_kernel(DecArgs a) {
     const uint32_t loff = valid ? (uint32_t)(lane * k) : 0u;
 
     // theta loads go out first; the Decoupled AdamW instances (3 blocks per
-    // CU, v read beside theta) load v first and theta after Q instead: a
-    // theta prefetch measured 13% slower there (1.506 against 1.329 ms on the
-    // OLMo2-1B half shard)
+    // CU, v read beside theta) load v first and theta after Q instead: with
+    // plain theta accesses a theta prefetch measured 13% slower there (1.506
+    // against 1.329 ms on the OLMo2-1B half shard)
     ThetaTile th;
     if constexpr (AD)
         prefetch_moment2(a, base, full, lane, th);
